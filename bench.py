@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the 4-bit codec and dequantize-and-multiply on one MI355X.
+
+Workload (LLM MLP up-projection): bf16 weight [14336, 4096], N(0, 0.02^2) with
+0.1 % entries scaled x20, NF4, block 64, double-quantized scales (8-bit, groups
+of 256, fp32 group scale, mean offset); x bf16 [1, 4096]; A bf16 [512, 4096].
+
+A step is one pass of the whole path on that weight: quantize_4bit ->
+double_quant -> dequantize_4bit (to bf16) -> gemv_4bit (M = 1) ->
+gemm_4bit (M = 512).  The headline value is gemv_4bit's achieved HBM
+bandwidth: algorithmic bytes per launch / average launch duration, timed with
+HIP events on the launch stream while rotating over distinct weight copies
+(> 512 MB, twice the 256 MB Infinity Cache) so the bytes come from HBM.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gemv_4bit achieved HBM GB/s (NF4, 14336x4096, M=1) + codec GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+N, K, BS, BS2, M_GEMV, M_GEMM = 14336, 4096, 64, 256, 1, 512
+ROTATE_BYTES = 640 << 20       # > 2 x 256 MB Infinity Cache
+
+
+def algorithmic_bytes():
+    """Bytes each op must move at this workload (intermediates excluded)."""
+    numel = N * K
+    nb = numel // BS
+    dq_state = nb + 4 * (-(-nb // BS2)) + 4 + 4 * 256     # codes, group scales, offset, table
+    packed = numel // 2
+    return {
+        "quantize_4bit+double_quant": 2 * numel + packed + dq_state,
+        "dequantize_4bit": packed + dq_state + 2 * numel,
+        "gemv_4bit": packed + dq_state + 2 * K * M_GEMV + 2 * N * M_GEMV,
+        "gemm_4bit": packed + dq_state + 2 * K * M_GEMM + 2 * N * M_GEMM,
+    }
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+GEMV_SOURCES = ["quantized_matvec_amd/csrc/qmv_gemv.hip", "quantized_matvec_amd/csrc/qmv_device.hpp"]
+
+
+def measured_traffic():
+    """HBM bytes per gemv launch from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemv_4bit_nf4_14336x4096_m1_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != source_hash(GEMV_SOURCES):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def timed_loop(fn, iters, stream, torch):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters * 1e3   # microseconds per call
+
+
+def cpu_baseline(W_cpu, x_cpu, budget_s=12.0):
+    """The oracle's gemv (scale reconstruction, dequantize, float64 matmul) on
+    a bounded sample of output rows, single-threaded."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    W64 = W_cpu.to(torch.float64).numpy()
+    x64 = x_cpu.to(torch.float64).numpy()
+    # the double-quant state needs every block scale of the weight
+    absmax = O.block_absmax(W64, BS).astype(np.float32)
+    q, a2, off = O.double_quant(absmax, BS2)
+    rows_done, t_used, chunk = 0, 0.0, 64
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s and rows_done + chunk <= N:
+            r = np.arange(rows_done, rows_done + chunk)
+            packed, _ = O.quantize_4bit(W64[r], BS, "nf4")      # codes of these rows (untimed)
+            nb0 = rows_done * K // BS
+            blocks = np.arange(nb0, nb0 + chunk * K // BS)
+            ts = time.perf_counter()
+            # scale reconstruction of these rows' blocks (their groups may straddle the chunk)
+            ahat = (O.linear8_table()[q[blocks]] * a2[blocks // BS2] + off).astype(np.float32)
+            O.matmul_4bit(x64, packed, ahat, chunk, K, BS, "nf4")
+            t_used += time.perf_counter() - ts
+            rows_done += chunk
+    per_row = (K // 2 + K // BS * (1 + 4 / BS2)) + 2      # packed + scales + y per row
+    gbs = rows_done * per_row / t_used / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} of {N} output rows of the gemv (dequantize + float64 matmul), "
+                      f"{t_used:.1f} s of single-threaded CPU time; same bytes-per-row accounting"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kernel-iters", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_matvec_amd import build as qbuild
+    from quantized_matvec_amd import qmv, synth
+    if not os.path.exists(qmv.library_path):
+        qbuild.build()
+    qmv.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)      # default priority
+    ab = algorithmic_bytes()
+
+    W_cpu = synth.weight(3, 0)                   # [14336, 4096] bf16 with outliers
+    x_cpu = synth.activations(3, 0, M_GEMV)
+    A_cpu = synth.gaussian((M_GEMM, K), 1.0, 100 * 4 + 2, "bf16")
+
+    with torch.cuda.stream(stream):
+        W = W_cpu.to(dev)
+        x = x_cpu.to(dev)
+        A = A_cpu.to(dev)
+        packed0, st0 = qmv.quantize_4bit(W, BS, "nf4", double_quant=True, blocksize2=BS2)
+        # distinct copies so repeated launches stream from HBM, not the cache
+        n_w = max(2, -(-ROTATE_BYTES // (W.numel() * 2)))
+        n_p = max(2, -(-ROTATE_BYTES // packed0.numel()))
+        Ws = [W] + [W.clone() for _ in range(n_w - 1)]
+        packs = [packed0] + [packed0.clone() for _ in range(n_p - 1)]
+        states = [st0] + [qmv.QuantState(st0.shape, st0.dtype, BS, "nf4", None, st0.absmax_q.clone(),
+                                         st0.absmax2.clone(), st0.offset.clone(), st0.code2.clone(), BS2)
+                          for _ in range(n_p - 1)]
+        wout = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for _ in range(n_w)]
+        y = torch.empty(M_GEMV, N, dtype=torch.bfloat16, device=dev)
+        C = torch.empty(M_GEMM, N, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+        def step(i):
+            p, st = qmv.quantize_4bit(Ws[i % n_w], BS, "nf4", double_quant=True, blocksize2=BS2)
+            qmv.dequantize_4bit(p, st, out=wout[i % n_w])
+            qmv.gemv_4bit(x, p, st, out=y)
+            qmv.gemm_4bit(A, p, st, out=C)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        us_step = timed_loop(step, args.steps, stream, torch)
+        torch.cuda.synchronize()
+        wall_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+        kiters = args.kernel_iters
+        kern = {}
+
+        def run_gemv(i):
+            qmv.gemv_4bit(x, packs[i % n_p], states[i % n_p], out=y)
+
+        def run_gemm(i):
+            qmv.gemm_4bit(A, packs[i % n_p], states[i % n_p], out=C)
+
+        def run_deq(i):
+            qmv.dequantize_4bit(packs[i % n_p], states[i % n_p], out=wout[i % n_w])
+
+        qbuf = [torch.empty_like(packed0) for _ in range(n_w)]
+        abuf = [torch.empty_like(st0.absmax_q, dtype=torch.float32) for _ in range(n_w)]
+        L = qmv.lib()
+        s_h = stream.cuda_stream
+
+        def run_quant(i):      # the raw entry point (no allocation inside the loop)
+            L.qmv_quantize_4bit(Ws[i % n_w].data_ptr(), 2, N * K, BS, 0, qbuf[i % n_w].data_ptr(),
+                                abuf[i % n_w].data_ptr(), s_h)
+
+        dq_out = [(torch.empty_like(st0.absmax_q), torch.empty_like(st0.absmax2),
+                   torch.empty_like(st0.offset), torch.empty_like(st0.code2)) for _ in range(n_w)]
+        nbk = N * K // BS
+        ws = torch.empty(L.qmv_double_quant_workspace(nbk), dtype=torch.uint8, device=dev)
+
+        def run_dq(i):
+            q, a2, off, c2 = dq_out[i % n_w]
+            L.qmv_double_quant(abuf[i % n_w].data_ptr(), nbk, BS2, None, q.data_ptr(), a2.data_ptr(),
+                               off.data_ptr(), c2.data_ptr(), ws.data_ptr(), ws.numel(), s_h)
+
+        for name, fn, iters in (("gemv_4bit", run_gemv, kiters), ("gemm_4bit", run_gemm, kiters // 4),
+                                ("dequantize_4bit", run_deq, kiters // 4),
+                                ("quantize_4bit", run_quant, kiters // 4),
+                                ("double_quant", run_dq, kiters // 4)):
+            for i in range(5):
+                fn(i)
+            kern[name] = timed_loop(fn, iters, stream, torch)
+
+    rep = {}
+    for name, us in kern.items():
+        e = {"us_per_launch": round(us, 3)}
+        if name == "gemv_4bit" or name == "dequantize_4bit":
+            b = ab[name]
+            e.update(bytes=b, gbs=round(b / us / 1e3, 1), hbm_frac=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
+        elif name == "gemm_4bit":
+            fl = 2.0 * M_GEMM * N * K
+            e.update(flops=fl, tflops=round(fl / us / 1e6, 2),
+                     mfma_frac=round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4))
+        rep[name] = e
+    q_us = kern["quantize_4bit"] + kern["double_quant"]
+    b = ab["quantize_4bit+double_quant"]
+    rep["quantize_4bit+double_quant"] = {"us": round(q_us, 3), "bytes": b, "gbs": round(b / q_us / 1e3, 1),
+                                         "hbm_frac": round(b / q_us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    gemv_us = kern["gemv_4bit"]
+    gemv_gbs = ab["gemv_4bit"] / gemv_us / 1e3
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "LLM MLP up-projection 14336x4096 bf16 (0.1% x20 outliers), NF4 block 64, "
+                               "double-quantized scales (256-groups); gemv M=1, gemm M=512",
+                   "N": N, "K": K, "quant_type": "nf4", "blocksize": BS, "blocksize2": BS2,
+                   "gemv_M": M_GEMV, "gemm_M": M_GEMM, "parallelism": "single-gpu",
+                   "rotating_weight_copies": n_p},
+        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "gemv_4bit",
+                     "algorithmic_bytes_per_launch": ab["gemv_4bit"], "avg_launch_us": round(gemv_us, 3)},
+        "kernels": rep,
+        "step_wall_ms": round(wall_step_ms, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W_cpu, x_cpu)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

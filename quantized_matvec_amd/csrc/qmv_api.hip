@@ -1,0 +1,248 @@
+// The C ABI of libqmv.so (declared in include/qmv.h): argument validation on
+// the host, then a launch on the caller's stream.  Nothing here allocates,
+// synchronizes or falls back to another path.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <set>
+#include <vector>
+
+#include "qmv.h"
+#include "qmv_launch.hpp"
+
+using namespace qmv;
+
+namespace {
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int d) { return d == QMV_F32 || d == QMV_F16 || d == QMV_BF16; }
+bool valid_qt(int q) { return q == QMV_NF4 || q == QMV_FP4; }
+bool valid_blocksize(int64_t bs) { return is_pow2(bs) && bs >= 32 && bs <= 4096; }
+
+float bits_to_float(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// Significant bits of a finite nonzero double.
+int sig_bits(double d) {
+  int e;
+  double m = frexp(fabs(d), &e);  // m in [0.5, 1)
+  int bits = 0;
+  while (m != 0.0) {
+    m = m * 2.0;
+    const double ip = floor(m);
+    m -= ip;
+    ++bits;
+  }
+  return bits;
+}
+
+// Midpoint of two doubles if it is exact, else NaN.
+double exact_midpoint(double lo, double hi) {
+  const double s = lo + hi;
+  const double bb = s - lo;
+  const double err = (lo - (s - bb)) + (hi - bb);  // TwoSum error term
+  if (err != 0.0) return NAN;
+  return s * 0.5;  // halving is exact for these magnitudes
+}
+
+// Sorted distinct values of the 16-entry table and their midpoints.
+Midpoints4 table_midpoints(int qt) {
+  const uint32_t *bits = table_bits(qt);
+  std::set<double> vals;
+  for (int c = 0; c < 16; ++c) vals.insert((double)bits_to_float(bits[c]));  // +0 == -0
+  std::vector<double> v(vals.begin(), vals.end());
+  Midpoints4 m{};
+  for (size_t j = 0; j + 1 < v.size() && j < 15; ++j) m.mid[j] = exact_midpoint(v[j], v[j + 1]);
+  return m;
+}
+
+const Midpoints4 &midpoints(int qt) {
+  static const Midpoints4 nf4 = table_midpoints(QMV_NF4);
+  static const Midpoints4 fp4 = table_midpoints(QMV_FP4);
+  return qt == QMV_NF4 ? nf4 : fp4;
+}
+
+int check_scales(const qmv_absmax *s, Scales *out, bool *dq) {
+  if (!s) return QMV_ERR_INVALID_ARG;
+  const bool plain = s->absmax != nullptr;
+  const bool any_dq = s->absmax_q || s->absmax2 || s->code2 || s->offset;
+  const bool all_dq = s->absmax_q && s->absmax2 && s->code2 && s->offset;
+  if (plain == any_dq) return QMV_ERR_INVALID_ARG;  // exactly one form
+  if (!plain && !all_dq) return QMV_ERR_INVALID_ARG;
+  Scales sc{};
+  if (plain) {
+    if (!aligned16(s->absmax)) return QMV_ERR_ALIGNMENT;
+    sc.absmax = s->absmax;
+  } else {
+    if (!valid_blocksize(s->blocksize2)) return QMV_ERR_UNSUPPORTED;
+    if (!aligned16(s->absmax_q) || !aligned16(s->absmax2) || !aligned16(s->code2) ||
+        !aligned16(s->offset))
+      return QMV_ERR_ALIGNMENT;
+    sc.q = s->absmax_q;
+    sc.absmax2 = s->absmax2;
+    sc.code2 = s->code2;
+    sc.offset = s->offset;
+    sc.log2bs2 = log2_exact(s->blocksize2);
+  }
+  *out = sc;
+  *dq = !plain;
+  return QMV_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_ERR_LAUNCH; }
+
+int check_matmul(int64_t M, int64_t N, int64_t K, int32_t blocksize, int qt) {
+  if (M <= 0 || N <= 0 || K <= 0 || !valid_qt(qt)) return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize)) return QMV_ERR_UNSUPPORTED;
+  if (K % blocksize != 0 || K % 32 != 0) return QMV_ERR_UNSUPPORTED;
+  if (N > INT64_MAX / K || M > INT64_MAX / K || M > INT64_MAX / N) return QMV_ERR_INVALID_ARG;
+  return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmv_quantize_4bit(const void *W, qmv_dtype w_dtype, int64_t numel, int32_t blocksize,
+                      qmv_quant_type quant_type, uint8_t *packed, float *absmax, void *stream) {
+  if (!W || !packed || !absmax || numel <= 0 || !valid_dtype(w_dtype) || !valid_qt(quant_type))
+    return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize)) return QMV_ERR_UNSUPPORTED;
+  if (!aligned16(W) || !aligned16(packed) || !aligned16(absmax)) return QMV_ERR_ALIGNMENT;
+  const int nt = quant_type == QMV_NF4 ? 15 : 14;  // thresholds between distinct values
+  for (int j = 0; j < nt; ++j) {  // the exactness argument needs these
+    const double m = midpoints(quant_type).mid[j];
+    if (isnan(m) || m == 0.0 || sig_bits(m) > 29) return QMV_ERR_UNSUPPORTED;
+  }
+  return launch_status(launch_quantize_4bit(W, w_dtype, numel, log2_exact(blocksize), quant_type,
+                                            midpoints(quant_type), packed, absmax,
+                                            (hipStream_t)stream));
+}
+
+size_t qmv_double_quant_workspace(int64_t nblocks) {
+  return nblocks > 0 ? double_quant_workspace_bytes(nblocks) : 0;
+}
+
+int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
+                     const float *code2_host, uint8_t *absmax_q, float *absmax2, float *offset,
+                     float *code2_out, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!absmax || !absmax_q || !absmax2 || !offset || !code2_out || nblocks <= 0)
+    return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize2)) return QMV_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < double_quant_workspace_bytes(nblocks))
+    return QMV_ERR_WORKSPACE;
+  if (!aligned16(absmax) || !aligned16(absmax_q) || !aligned16(absmax2) || !aligned16(offset) ||
+      !aligned16(code2_out) || !aligned16(workspace))
+    return QMV_ERR_ALIGNMENT;
+  Code2Table t{};
+  if (code2_host) {
+    memcpy(t.v, code2_host, sizeof(t.v));
+  } else {
+    qmv_default_code2(t.v);
+  }
+  for (int k = 0; k < 256; ++k)
+    if (!isfinite(t.v[k])) return QMV_ERR_INVALID_ARG;
+  for (int k = 0; k + 1 < 256; ++k) {
+    if (!(t.v[k] < t.v[k + 1])) return QMV_ERR_UNSUPPORTED;  // strictly increasing
+    const double m = exact_midpoint((double)t.v[k], (double)t.v[k + 1]);
+    if (isnan(m) || m == 0.0 || sig_bits(m) > 29) return QMV_ERR_UNSUPPORTED;
+  }
+  return launch_status(launch_double_quant(absmax, nblocks, log2_exact(blocksize2), t, absmax_q,
+                                           absmax2, offset, code2_out,
+                                           static_cast<double *>(workspace),
+                                           (hipStream_t)stream));
+}
+
+int qmv_dequantize_absmax(const qmv_absmax *scales, int64_t nblocks, float *absmax_out,
+                          void *stream) {
+  if (!absmax_out || nblocks <= 0) return QMV_ERR_INVALID_ARG;
+  Scales sc;
+  bool dq;
+  int rc = check_scales(scales, &sc, &dq);
+  if (rc != QMV_OK) return rc;
+  if (!aligned16(absmax_out)) return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_dequantize_absmax(sc, dq, nblocks, absmax_out, (hipStream_t)stream));
+}
+
+int qmv_dequantize_4bit(const uint8_t *packed, const qmv_absmax *scales, int64_t numel,
+                        int32_t blocksize, qmv_quant_type quant_type, void *out,
+                        qmv_dtype out_dtype, void *stream) {
+  if (!packed || !out || numel <= 0 || !valid_qt(quant_type) || !valid_dtype(out_dtype))
+    return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize)) return QMV_ERR_UNSUPPORTED;
+  Scales sc;
+  bool dq;
+  int rc = check_scales(scales, &sc, &dq);
+  if (rc != QMV_OK) return rc;
+  if (!aligned16(packed) || !aligned16(out)) return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_dequantize_4bit(packed, sc, dq, numel, log2_exact(blocksize),
+                                              quant_type, out, out_dtype, (hipStream_t)stream));
+}
+
+int qmv_gemv_4bit(const void *x, qmv_dtype x_dtype, int32_t M, int64_t N, int64_t K,
+                  const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
+                  qmv_quant_type quant_type, void *y, qmv_dtype y_dtype, void *stream) {
+  if (!x || !packed || !y || !valid_dtype(x_dtype) || !valid_dtype(y_dtype))
+    return QMV_ERR_INVALID_ARG;
+  int rc = check_matmul(M, N, K, blocksize, quant_type);
+  if (rc != QMV_OK) return rc;
+  if (M > 8) return QMV_ERR_UNSUPPORTED;
+  Scales sc;
+  bool dq;
+  rc = check_scales(scales, &sc, &dq);
+  if (rc != QMV_OK) return rc;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_gemv_4bit(x, x_dtype, M, N, K, packed, sc, dq, log2_exact(blocksize),
+                                        quant_type, y, y_dtype, (hipStream_t)stream));
+}
+
+int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_t K,
+                  const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
+                  qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, void *stream) {
+  if (!A || !packed || !C || !valid_dtype(a_dtype) || !valid_dtype(c_dtype))
+    return QMV_ERR_INVALID_ARG;
+  int rc = check_matmul(M, N, K, blocksize, quant_type);
+  if (rc != QMV_OK) return rc;
+  if (a_dtype != QMV_BF16) return QMV_ERR_UNSUPPORTED;
+  if ((M + 127) / 128 > 65535) return QMV_ERR_UNSUPPORTED;
+  Scales sc;
+  bool dq;
+  rc = check_scales(scales, &sc, &dq);
+  if (rc != QMV_OK) return rc;
+  if (!aligned16(A) || !aligned16(packed) || !aligned16(C)) return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_gemm_4bit(A, M, N, K, packed, sc, dq, log2_exact(blocksize),
+                                        quant_type, C, c_dtype, (hipStream_t)stream));
+}
+
+int qmv_code_table(qmv_quant_type quant_type, float out16[16]) {
+  if (!out16 || !valid_qt(quant_type)) return QMV_ERR_INVALID_ARG;
+  const uint32_t *bits = table_bits(quant_type);
+  for (int c = 0; c < 16; ++c) out16[c] = bits_to_float(bits[c]);
+  return QMV_OK;
+}
+
+int qmv_default_code2(float out256[256]) {
+  if (!out256) return QMV_ERR_INVALID_ARG;
+  for (int k = 0; k < 256; ++k) out256[k] = (float)(k - 127) / 127.0f;  // correctly rounded
+  return QMV_OK;
+}
+
+const char *qmv_status_string(int status) {
+  switch (status) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_INVALID_ARG: return "invalid argument";
+    case QMV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QMV_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case QMV_ERR_LAUNCH: return "kernel launch failed";
+    case QMV_ERR_HIP: return "HIP runtime error";
+    case QMV_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device-side building blocks shared by the codec, gemv and gemm kernels.
+//
+// Code tables, scale decoding and number-format conversions for gfx950.  All
+// arithmetic that the codec's bit-exact contract depends on is compiled with
+// floating-point contraction off, so no multiply-add fusion can change a
+// result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+enum : int { kNF4 = 0, kFP4 = 1 };
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// NF4 values in fp32, by code (ascending).  The 16 numbers are the QLoRA
+// normal-quantile construction: 8 positive and 7 negative quantiles of N(0,1)
+// at evenly spaced probabilities between 1/2 and 0.9677083, plus 0, divided by
+// the largest and rounded once to fp32.
+constexpr uint32_t kNF4Bits[16] = {
+    0xbf800000u, 0xbf3239b3u, 0xbf066b30u, 0xbeca32a0u, 0xbe91a24cu, 0xbe3d353fu,
+    0xbdba786bu, 0x00000000u, 0x3da2fb03u, 0x3e24cae1u, 0x3e7c04dcu, 0x3ead0338u,
+    0x3ee1a4b7u, 0x3f1007aau, 0x3f3913b1u, 0x3f800000u};
+
+// FP4 values in fp32, by code: E2M1 (bits s e1 e0 m) divided by 6, so the
+// magnitudes are 0, 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1; code 8 is -0.
+constexpr uint32_t kFP4Bits[16] = {
+    0x00000000u, 0x3daaaaabu, 0x3e2aaaabu, 0x3e800000u, 0x3eaaaaabu, 0x3f000000u,
+    0x3f2aaaabu, 0x3f800000u, 0x80000000u, 0xbdaaaaabu, 0xbe2aaaabu, 0xbe800000u,
+    0xbeaaaaabu, 0xbf000000u, 0xbf2aaaabu, 0xbf800000u};
+
+__host__ __device__ inline const uint32_t *table_bits(int qt) {
+  return qt == kNF4 ? kNF4Bits : kFP4Bits;
+}
+
+// Kernel-argument form of the per-block scales (plain or double-quantized).
+struct Scales {
+  const float *absmax;    // plain fp32 scales
+  const uint8_t *q;       // DQ: 8-bit codes
+  const float *absmax2;   // DQ: group scales
+  const float *code2;     // DQ: 256-entry table
+  const float *offset;    // DQ: subtracted mean
+  int log2bs2;            // DQ: log2(group size)
+};
+
+// Scale of block b.  With double quantization:
+// fp32(fp32(code2[q[b]] * absmax2[b / bs2]) + offset), two roundings.
+template <bool DQ>
+__device__ __forceinline__ float block_scale(const Scales &s, int64_t b) {
+  if constexpr (!DQ) {
+    return s.absmax[b];
+  } else {
+#pragma clang fp contract(off)
+    const float c = s.code2[s.q[b]];
+    const float g = s.absmax2[b >> s.log2bs2];
+    const float p = c * g;   // rounded to fp32 on its own: never fused with the add
+    return p + s.offset[0];
+  }
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Pins an fp32 value in a register so the backend cannot merge the
+// instruction that produced it with the one that consumes it (for instance a
+// multiply followed by an fp16 conversion becoming one mixed-precision FMA
+// with a single rounding, which also turns -0 into +0).
+__device__ __forceinline__ float materialize(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 on an fp32 input).
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)materialize(f));
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t f32_to_bits16(float f) {
+  if constexpr (DT == kBF16) return f32_to_bf16_rne(f);
+  else return f32_to_f16_rne(f);
+}
+
+template <int DT>
+__device__ __forceinline__ float bits16_to_f32(uint32_t h) {
+  if constexpr (DT == kBF16) return bf16_bits_to_f32(h);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Element storage type per dtype tag.
+template <int DT> struct Storage;
+template <> struct Storage<kF32> { using type = float; };
+template <> struct Storage<kF16> { using type = uint16_t; };
+template <> struct Storage<kBF16> { using type = uint16_t; };
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const typename Storage<DT>::type *p, int64_t i) {
+  if constexpr (DT == kF32) return p[i];
+  else return bits16_to_f32<DT>(p[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(typename Storage<DT>::type *p, int64_t i, float v) {
+  if constexpr (DT == kF32) p[i] = v;
+  else p[i] = (uint16_t)f32_to_bits16<DT>(v);
+}
+
+}  // namespace qmv

@@ -1,0 +1,50 @@
+// Host-side launchers of the HIP kernels (internal to libqmv.so).  Each
+// launcher assumes its arguments were validated by the C ABI layer and only
+// maps them onto a grid; it returns the status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmv_device.hpp"
+
+namespace qmv {
+
+// Midpoints of adjacent distinct values of a sorted code table, exact in
+// float64; the encoder compares x against absmax * mid[j].  NF4 uses all 15,
+// FP4 (whose +0 and -0 are one value) the first 14.
+struct Midpoints4 {
+  double mid[15];
+};
+
+struct Code2Table {
+  float v[256];
+};
+
+int log2_exact(int64_t v);  // log2 of a power of two
+
+hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int log2bs, int qt,
+                                const Midpoints4 &mids, uint8_t *packed, float *absmax,
+                                hipStream_t st);
+
+size_t double_quant_workspace_bytes(int64_t nblocks);
+
+hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,
+                               const Code2Table &code2, uint8_t *q, float *absmax2,
+                               float *offset, float *code2_out, double *ws, hipStream_t st);
+
+hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t nblocks, float *out,
+                                    hipStream_t st);
+
+hipError_t launch_dequantize_4bit(const uint8_t *packed, const Scales &sc, bool dq, int64_t numel,
+                                  int log2bs, int qt, void *out, int out_dtype, hipStream_t st);
+
+hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_t K,
+                            const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
+                            void *y, int y_dtype, hipStream_t st);
+
+hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
+                            const Scales &sc, bool dq, int log2bs, int qt, void *C, int c_dtype,
+                            hipStream_t st);
+
+}  // namespace qmv

@@ -1,0 +1,251 @@
+"""Python binding of libqmv.so (ctypes).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, and every step of every operation runs in the library's HIP kernels.
+There is no CPU or PyTorch fallback; if the library is not built, or a call's
+arguments are refused, these functions raise.
+
+Names follow the op set of the pages ("Feat/mps gemm 4bit bf16", table "What
+runs natively now"; "mps-bitsandbytes 0.4.7", section "Functional API").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "QmvError", "QuantState", "lib", "library_path", "quantize_4bit", "double_quant",
+    "dequantize_absmax", "dequantize_4bit", "gemv_4bit", "gemm_4bit", "code_table",
+    "default_code2", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libqmv.so")
+
+STATUS = {0: "QMV_OK", -1: "QMV_ERR_INVALID_ARG", -2: "QMV_ERR_UNSUPPORTED",
+          -3: "QMV_ERR_ALIGNMENT", -4: "QMV_ERR_LAUNCH", -5: "QMV_ERR_HIP",
+          -6: "QMV_ERR_WORKSPACE"}
+_QT = {"nf4": 0, "fp4": 1}
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_string(status)})")
+
+
+class _Absmax(ctypes.Structure):
+    _fields_ = [("absmax", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
+                ("absmax2", ctypes.c_void_p), ("code2", ctypes.c_void_p),
+                ("offset", ctypes.c_void_p), ("blocksize2", ctypes.c_int32)]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(library_path):
+        raise ImportError(f"{library_path} is missing: build it with "
+                          "`python -m quantized_matvec_amd.build`")
+    L = ctypes.CDLL(library_path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    ap = ctypes.POINTER(_Absmax)
+    sig = {
+        "qmv_quantize_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, ctypes.c_int, vp, vp, vp]),
+        "qmv_double_quant_workspace": (sz, [i64]),
+        "qmv_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "qmv_dequantize_absmax": (ctypes.c_int, [ap, i64, vp, vp]),
+        "qmv_dequantize_4bit": (ctypes.c_int, [vp, ap, i64, i32, ctypes.c_int, vp, ctypes.c_int, vp]),
+        "qmv_gemv_4bit": (ctypes.c_int, [vp, ctypes.c_int, i32, i64, i64, vp, ap, i32,
+                                         ctypes.c_int, vp, ctypes.c_int, vp]),
+        "qmv_gemm_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
+                                         ctypes.c_int, vp, ctypes.c_int, vp]),
+        "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
+        "qmv_default_code2": (ctypes.c_int, [vp]),
+        "qmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _LIB = L
+    return L
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().qmv_status_string(status).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise QmvError(rc, what)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    """Contiguous, 16-byte aligned device tensor (clones views that are not)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous() or t.data_ptr() % 16:
+        t = t.contiguous().clone()
+    return t
+
+
+@dataclass
+class QuantState:
+    """Everything dequantize / gemv / gemm need besides the packed codes."""
+    shape: tuple
+    dtype: torch.dtype
+    blocksize: int
+    quant_type: str
+    absmax: Optional[torch.Tensor] = None        # plain fp32 scales
+    absmax_q: Optional[torch.Tensor] = None      # double-quantized scales
+    absmax2: Optional[torch.Tensor] = None
+    offset: Optional[torch.Tensor] = None
+    code2: Optional[torch.Tensor] = None
+    blocksize2: int = 256
+
+    @property
+    def numel(self) -> int:
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    @property
+    def nblocks(self) -> int:
+        return -(-self.numel // self.blocksize)
+
+    @property
+    def double_quant(self) -> bool:
+        return self.absmax is None
+
+    def _c(self) -> _Absmax:
+        if self.absmax is not None:
+            return _Absmax(self.absmax.data_ptr(), None, None, None, None, 0)
+        return _Absmax(None, self.absmax_q.data_ptr(), self.absmax2.data_ptr(),
+                       self.code2.data_ptr(), self.offset.data_ptr(), self.blocksize2)
+
+
+def quantize_4bit(W: torch.Tensor, blocksize: int = 64, quant_type: str = "nf4",
+                  double_quant: bool = False, blocksize2: int = 256,
+                  code2: Optional[list] = None):
+    """Returns (packed uint8 [ceil(numel/2)], QuantState)."""
+    W = _dev(W, "W")
+    numel = W.numel()
+    packed = torch.empty((numel + 1) // 2, dtype=torch.uint8, device=W.device)
+    absmax = torch.empty(-(-numel // blocksize), dtype=torch.float32, device=W.device)
+    _check(lib().qmv_quantize_4bit(W.data_ptr(), _DT[W.dtype], numel, blocksize, _QT[quant_type],
+                                   packed.data_ptr(), absmax.data_ptr(), _stream(W)),
+           "quantize_4bit")
+    state = QuantState(tuple(W.shape), W.dtype, blocksize, quant_type, absmax=absmax)
+    if double_quant:
+        q, a2, off, c2 = _double_quant(absmax, blocksize2, code2)
+        state = QuantState(tuple(W.shape), W.dtype, blocksize, quant_type, None, q, a2, off, c2,
+                           blocksize2)
+    return packed, state
+
+
+def _double_quant(absmax: torch.Tensor, blocksize2: int = 256, code2: Optional[list] = None):
+    """Returns (absmax_q uint8, absmax2 fp32, offset fp32 [1], code2 fp32 [256])."""
+    absmax = _dev(absmax, "absmax")
+    n = absmax.numel()
+    dev = absmax.device
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    a2 = torch.empty(-(-n // blocksize2), dtype=torch.float32, device=dev)
+    off = torch.empty(1, dtype=torch.float32, device=dev)
+    c2 = torch.empty(256, dtype=torch.float32, device=dev)
+    wsb = lib().qmv_double_quant_workspace(n)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    host = None
+    if code2 is not None:
+        host = (ctypes.c_float * 256)(*[float(v) for v in code2])
+    _check(lib().qmv_double_quant(absmax.data_ptr(), n, blocksize2,
+                                  ctypes.cast(host, ctypes.c_void_p) if host is not None else None,
+                                  q.data_ptr(), a2.data_ptr(), off.data_ptr(), c2.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream(absmax)), "double_quant")
+    return q, a2, off, c2
+
+
+double_quant = _double_quant
+
+
+def dequantize_absmax(state: QuantState) -> torch.Tensor:
+    ref = state.absmax if state.absmax is not None else state.absmax_q
+    out = torch.empty(state.nblocks, dtype=torch.float32, device=ref.device)
+    c = state._c()
+    _check(lib().qmv_dequantize_absmax(ctypes.byref(c), state.nblocks, out.data_ptr(),
+                                       _stream(ref)), "dequantize_absmax")
+    return out
+
+
+def dequantize_4bit(packed: torch.Tensor, state: QuantState, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    packed = _dev(packed, "packed")
+    if out is None:
+        out = torch.empty(state.shape, dtype=out_dtype or state.dtype, device=packed.device)
+    elif not out.is_contiguous() or out.numel() != state.numel or out.data_ptr() % 16:
+        raise ValueError("out must be contiguous, 16-byte aligned and hold numel elements")
+    c = state._c()
+    _check(lib().qmv_dequantize_4bit(packed.data_ptr(), ctypes.byref(c), state.numel,
+                                     state.blocksize, _QT[state.quant_type], out.data_ptr(),
+                                     _DT[out.dtype], _stream(packed)), "dequantize_4bit")
+    return out
+
+
+def _matmul(name, x, packed, state, out, out_dtype):
+    if len(state.shape) != 2:
+        raise ValueError("the quantized weight must be 2-D [N, K]")
+    N, K = state.shape
+    packed = _dev(packed, "packed")
+    x = _dev(x, "x")
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or x.dtype, device=x.device)
+    elif not out.is_contiguous() or out.numel() != M * N or out.data_ptr() % 16:
+        raise ValueError("out must be contiguous, 16-byte aligned and hold M * N elements")
+    c = state._c()
+    f = getattr(lib(), "qmv_" + name)
+    _check(f(x2.data_ptr(), _DT[x2.dtype], M, N, K, packed.data_ptr(), ctypes.byref(c),
+             state.blocksize, _QT[state.quant_type], out.data_ptr(), _DT[out.dtype],
+             _stream(x2)), name)
+    return out
+
+
+def gemv_4bit(x: torch.Tensor, packed: torch.Tensor, state: QuantState,
+              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None):
+    """y [M, N] = x [M, K] @ W_hat^T for 1 <= M <= 8."""
+    return _matmul("gemv_4bit", x, packed, state, out, out_dtype)
+
+
+def gemm_4bit(A: torch.Tensor, packed: torch.Tensor, state: QuantState,
+              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None):
+    """C [M, N] = A [M, K] @ W_hat^T (A in bf16)."""
+    return _matmul("gemm_4bit", A, packed, state, out, out_dtype)
+
+
+def code_table(quant_type: str = "nf4") -> list:
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qmv_code_table(_QT[quant_type], ctypes.cast(buf, ctypes.c_void_p)), "code_table")
+    return list(buf)
+
+
+def default_code2() -> list:
+    buf = (ctypes.c_float * 256)()
+    _check(lib().qmv_default_code2(ctypes.cast(buf, ctypes.c_void_p)), "default_code2")
+    return list(buf)

@@ -30,3 +30,12 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def qmvlib():
+    """The built C-ABI library (built in-tree first if nothing is built yet)."""
+    from quantized_matvec_amd import build, qmv
+    if not os.path.exists(qmv.library_path):
+        build.build()
+    return qmv.lib()

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: every symbol include/qmv.h declares is exported,
+the host-side tables match the oracle bit for bit, and every precondition
+comes back as its status code before anything is launched.
+
+Pointers below are fake but well-formed host integers: validation rejects the
+call before any HIP runtime call, so nothing is dereferenced."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from quantized_matvec_amd import qmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH, HIPERR, WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+P = 0x7F0000010000          # 16-byte aligned fake device address
+P2 = P + 0x100000
+MIS = P + 4                 # misaligned
+F32, F16, BF16 = 0, 1, 2
+NF4, FP4 = 0, 1
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "qmv.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(qmvlib):
+    names = header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(qmvlib, n), n
+
+
+def test_code_tables_match_oracle_bits(qmvlib):
+    for qt in ("nf4", "fp4"):
+        got = np.array(qmv.code_table(qt), dtype=np.float32)
+        assert got.view(np.uint32).tolist() == O.code_table(qt).view(np.uint32).tolist()
+    got = np.array(qmv.default_code2(), dtype=np.float32)
+    assert got.view(np.uint32).tolist() == O.linear8_table().view(np.uint32).tolist()
+
+
+def test_status_strings(qmvlib):
+    for s in (OK, INVALID, UNSUPPORTED, ALIGN, LAUNCH, HIPERR, WORKSPACE):
+        assert qmvlib.qmv_status_string(s)
+    assert qmvlib.qmv_status_string(12345) == b"unknown status"
+    assert qmvlib.qmv_code_table(7, None) == INVALID
+
+
+def _scales(absmax=0, q=0, a2=0, code2=0, off=0, bs2=256):
+    return qmv._Absmax(absmax or None, q or None, a2 or None, code2 or None, off or None, bs2)
+
+
+def test_quantize_preconditions(qmvlib):
+    f = qmvlib.qmv_quantize_4bit
+    assert f(None, F32, 64, 64, NF4, P, P2, None) == INVALID
+    assert f(P, F32, 0, 64, NF4, P, P2, None) == INVALID
+    assert f(P, 9, 64, 64, NF4, P, P2, None) == INVALID
+    assert f(P, F32, 64, 64, 5, P, P2, None) == INVALID
+    for bs in (16, 48, 8192, 0, -64):
+        assert f(P, BF16, 64, bs, NF4, P, P2, None) == UNSUPPORTED
+    assert f(MIS, BF16, 64, 64, NF4, P, P2, None) == ALIGN
+    assert f(P, BF16, 64, 64, NF4, MIS, P2, None) == ALIGN
+
+
+def test_double_quant_preconditions(qmvlib):
+    f = qmvlib.qmv_double_quant
+    ws = qmvlib.qmv_double_quant_workspace(1000)
+    assert ws == 8 * (4 + 1)
+    assert qmvlib.qmv_double_quant_workspace(0) == 0
+    args = lambda **k: dict(dict(a=P, n=1000, bs2=256, code=None, q=P, a2=P, off=P, c2o=P, w=P2, wsb=ws), **k)
+    call = lambda d: f(d["a"], d["n"], d["bs2"], d["code"], d["q"], d["a2"], d["off"], d["c2o"], d["w"], d["wsb"], None)
+    assert call(args(n=0)) == INVALID
+    assert call(args(a=0)) == INVALID
+    assert call(args(bs2=100)) == UNSUPPORTED
+    assert call(args(wsb=ws - 1)) == WORKSPACE
+    assert call(args(w=0)) == WORKSPACE
+    assert call(args(q=MIS)) == ALIGN
+    bad = (ctypes.c_float * 256)(*([0.0] * 256))                # not increasing
+    assert call(args(code=ctypes.cast(bad, ctypes.c_void_p))) == UNSUPPORTED
+    nan = (ctypes.c_float * 256)(*[float("nan")] + list(np.linspace(0, 1, 255)))
+    assert call(args(code=ctypes.cast(nan, ctypes.c_void_p))) == INVALID
+    wide = np.linspace(-1, 1, 256).astype(np.float32)
+    wide[0] = np.float32(-1e30)                                   # midpoint not exact
+    w = (ctypes.c_float * 256)(*wide.tolist())
+    assert call(args(code=ctypes.cast(w, ctypes.c_void_p))) == UNSUPPORTED
+    sym = np.linspace(-1, 1, 256).astype(np.float32)              # zero midpoint (+-v)
+    s = (ctypes.c_float * 256)(*sym.tolist())
+    assert call(args(code=ctypes.cast(s, ctypes.c_void_p))) == UNSUPPORTED
+
+
+def test_scale_descriptor_preconditions(qmvlib):
+    f = qmvlib.qmv_dequantize_4bit
+    ok_plain = _scales(absmax=P2)
+    both = _scales(absmax=P2, q=P, a2=P, code2=P, off=P)
+    neither = _scales()
+    partial = _scales(q=P, a2=P)
+    bad_bs2 = _scales(q=P, a2=P, code2=P, off=P, bs2=100)
+    mis = _scales(q=P, a2=MIS, code2=P, off=P)
+    assert f(P, None, 64, 64, NF4, P, BF16, None) == INVALID
+    for sc, want in ((both, INVALID), (neither, INVALID), (partial, INVALID),
+                     (bad_bs2, UNSUPPORTED), (mis, ALIGN)):
+        assert f(P, ctypes.byref(sc), 64, 64, NF4, P, BF16, None) == want
+    assert f(P, ctypes.byref(ok_plain), 64, 48, NF4, P, BF16, None) == UNSUPPORTED
+    assert f(P, ctypes.byref(ok_plain), 64, 64, NF4, P, 3, None) == INVALID
+    assert f(P, ctypes.byref(ok_plain), -1, 64, NF4, P, BF16, None) == INVALID
+    assert f(MIS, ctypes.byref(ok_plain), 64, 64, NF4, P, BF16, None) == ALIGN
+    g = qmvlib.qmv_dequantize_absmax
+    assert g(ctypes.byref(both), 10, P, None) == INVALID
+    assert g(ctypes.byref(ok_plain), 0, P, None) == INVALID
+
+
+def test_matmul_preconditions(qmvlib):
+    sc = _scales(absmax=P2)
+    gv, gm = qmvlib.qmv_gemv_4bit, qmvlib.qmv_gemm_4bit
+    r = ctypes.byref(sc)
+    assert gv(P, BF16, 9, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # M > 8
+    assert gv(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
+    assert gv(P, BF16, 1, 0, 64, P, r, 64, NF4, P, BF16, None) == INVALID
+    assert gv(P, BF16, 1, 64, 96, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # K % bs
+    assert gv(P, BF16, 1, 64, 48, P, r, 32, NF4, P, BF16, None) == UNSUPPORTED   # K % 32
+    assert gv(P, BF16, 1, 64, 64, P, r, 64, NF4, MIS, BF16, None) == ALIGN
+    assert gv(None, BF16, 1, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
+    assert gm(P, F32, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED    # A must be bf16
+    assert gm(P, BF16, 8, 64, 64, P, r, 100, NF4, P, BF16, None) == UNSUPPORTED
+    assert gm(P, BF16, 8, 64, 64, P, None, 64, NF4, P, BF16, None) == INVALID
+    assert gm(P, BF16, 8, 64, 64, P, r, 64, 2, P, BF16, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors(qmvlib):
+    import torch
+    with pytest.raises(ValueError):
+        qmv.quantize_4bit(torch.zeros(64))

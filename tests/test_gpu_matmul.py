@@ -1,0 +1,166 @@
+"""GPU parity of gemv_4bit and gemm_4bit against the CPU oracle (dequantize,
+then a float64 matmul), through the C ABI.
+
+Tolerances (relative L2 over the compared outputs): 1e-3 for fp32 outputs and
+2e-2 for bf16 / fp16 outputs.  Exact pins: a one-hot x returns a column of
+the dequantized weight bit for bit (fp32 path), and identity rows of A return
+rows of the bf16-rounded dequantized weight bit for bit (gemm)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from quantized_matvec_amd import qmv, synth
+
+pytestmark = pytest.mark.gpu
+TDT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+TOL = {"fp32": 1e-3, "fp16": 2e-2, "bf16": 2e-2}
+
+
+def f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def oracle_state(W64, bs, qt, dq, bs2=256):
+    """Oracle quantization of the whole weight: (packed, a_hat)."""
+    packed, absmax = O.quantize_4bit(W64, bs, qt)
+    if dq:
+        q, a2, off = O.double_quant(absmax, bs2)
+        return packed, O.dequant_absmax(q, a2, off, None, bs2)
+    return packed, absmax
+
+
+def upload_state(packed, absmax, shape, dtype, bs, qt):
+    st = qmv.QuantState(tuple(shape), dtype, bs, qt, absmax=torch.from_numpy(absmax).cuda())
+    return torch.from_numpy(packed).cuda(), st
+
+
+def gaussian(shape, sigma, seed, dtype):
+    return synth.gaussian(shape, sigma, seed, dtype)
+
+
+# ---------------------------------------------------------------- gemv
+def test_gemv_config1_fp32():
+    """1024 x 1024 fp32 weight N(0, 0.02^2), NF4 block 64, fp32 x and y."""
+    W = synth.weight(1)
+    x = synth.activations(1)
+    packed, st = qmv.quantize_4bit(W.cuda(), 64, "nf4")
+    y = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
+    p_ref, a_ref = O.quantize_4bit(f64(W), 64, "nf4")
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    ref = O.matmul_4bit(f64(x), p_ref, a_ref, 1024, 1024, 64, "nf4")
+    assert rel_l2(f64(y), ref) <= 1e-3
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_gemv_one_hot_returns_column_exactly(qt):
+    N, K = 257, 2048
+    W = gaussian((N, K), 0.02, 5, "fp32")
+    p_ref, a_ref = O.quantize_4bit(f64(W), 64, qt)
+    packed, st = upload_state(p_ref, a_ref, (N, K), torch.float32, 64, qt)
+    What = O.dequantize_4bit(p_ref, a_ref, N * K, 64, qt).reshape(N, K)
+    for k in (0, 31, 1000, K - 1):
+        x = torch.zeros(1, K)
+        x[0, k] = 1.0
+        y = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(y[0].view(np.uint32), What[:, k].view(np.uint32))
+
+
+def test_gemv_config2_bf16():
+    """4096 x 4096 bf16 weight, NF4 block 64, fp32 scales, bf16 x and y."""
+    W = synth.weight(2)
+    x = synth.activations(2)
+    p_ref, a_ref = O.quantize_4bit(f64(W), 64, "nf4")
+    packed, st = qmv.quantize_4bit(W.cuda(), 64, "nf4")
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    y = qmv.gemv_4bit(x.cuda(), packed, st)
+    assert y.dtype == torch.bfloat16
+    ref = O.matmul_4bit(f64(x), p_ref, a_ref, 4096, 4096, 64, "nf4")
+    assert rel_l2(f64(y), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("qt,dq", [("nf4", False), ("fp4", True)])
+def test_gemv_all_m_ragged_n(M, qt, dq):
+    N, K, bs = 333, 4096 + 512, 128
+    W = gaussian((N, K), 0.02, 10 + M, "bf16")
+    x = gaussian((M, K), 1.0, 20 + M, "bf16")
+    p_ref, ahat = oracle_state(f64(W), bs, qt, dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, qt, double_quant=dq)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    y = qmv.gemv_4bit(x.cuda(), packed, st)
+    ref = O.matmul_4bit(f64(x), p_ref, ahat, N, K, bs, qt)
+    assert rel_l2(f64(y), ref) <= 2e-2
+    yf = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
+    assert rel_l2(f64(yf), ref) <= 1e-2      # bf16 x / table rounding only
+
+
+@pytest.mark.parametrize("xd,yd", [("fp32", "fp32"), ("fp16", "fp16"), ("fp16", "fp32"),
+                                   ("bf16", "fp32"), ("fp32", "bf16")])
+def test_gemv_dtypes(xd, yd):
+    N, K = 130, 1024
+    W = gaussian((N, K), 0.02, 3, "bf16")
+    x = gaussian((2, K), 1.0, 4, xd)
+    p_ref, a_ref = O.quantize_4bit(f64(W), 64, "nf4")
+    packed, st = upload_state(p_ref, a_ref, (N, K), torch.bfloat16, 64, "nf4")
+    y = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=TDT[yd])
+    ref = O.matmul_4bit(f64(x), p_ref, a_ref, N, K, 64, "nf4")
+    tol = 1e-3 if (xd, yd) == ("fp32", "fp32") else 2e-2
+    assert rel_l2(f64(y), ref) <= tol
+
+
+def test_gemv_minimal_shapes():
+    for N, K in ((1, 32), (5, 64), (64, 96)):
+        W = gaussian((N, K), 0.02, N, "bf16")
+        x = gaussian((1, K), 1.0, K, "fp32")
+        p_ref, a_ref = O.quantize_4bit(f64(W), 32, "nf4")
+        packed, st = upload_state(p_ref, a_ref, (N, K), torch.bfloat16, 32, "nf4")
+        y = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
+        ref = O.matmul_4bit(f64(x), p_ref, a_ref, N, K, 32, "nf4")
+        assert rel_l2(f64(y), ref) <= 1e-3
+
+
+# ---------------------------------------------------------------- gemm
+@pytest.mark.parametrize("M", [1, 8, 100, 128, 300])
+@pytest.mark.parametrize("qt,dq", [("nf4", False), ("fp4", True)])
+def test_gemm_full_output(M, qt, dq):
+    N, K, bs = 1000, 1024 + 64, 64
+    W = gaussian((N, K), 0.02, 7, "bf16")
+    A = gaussian((M, K), 1.0, 8, "bf16")
+    p_ref, ahat = oracle_state(f64(W), bs, qt, dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, qt, double_quant=dq)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    C = qmv.gemm_4bit(A.cuda(), packed, st)
+    ref = O.matmul_4bit(f64(A), p_ref, ahat, N, K, bs, qt)
+    assert rel_l2(f64(C), ref) <= 2e-2
+    Cf = qmv.gemm_4bit(A.cuda(), packed, st, out_dtype=torch.float32)
+    assert rel_l2(f64(Cf), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_gemm_identity_rows_exact(qt):
+    N, K = 300, 256
+    W = gaussian((N, K), 0.02, 9, "bf16")
+    p_ref, a_ref = O.quantize_4bit(f64(W), 64, qt)
+    packed, st = upload_state(p_ref, a_ref, (N, K), torch.bfloat16, 64, qt)
+    A = torch.eye(K, dtype=torch.bfloat16)[:200]
+    C = qmv.gemm_4bit(A.cuda(), packed, st).cpu()
+    What = O.dequantize_4bit(p_ref, a_ref, N * K, 64, qt, "bf16").reshape(N, K)
+    got = C.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, What[:, :200].T)
+
+
+def test_gemm_m1_matches_gemv():
+    N, K = 4096, 4096
+    W = gaussian((N, K), 0.02, 11, "bf16")
+    x = gaussian((1, K), 1.0, 12, "bf16")
+    packed, st = qmv.quantize_4bit(W.cuda(), 64, "nf4")
+    y1 = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
+    y2 = qmv.gemm_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
+    assert rel_l2(f64(y2), f64(y1)) <= 1e-2
