@@ -3,19 +3,499 @@
 // ("Feat/mps gemm 4bit bf16", table "What runs natively now": gemv_4bit is a
 // fused dequant + dot for the decode step).
 //
-// Data flow: a wave owns one weight row at a time; each lane streams 16-byte
-// pieces of the packed row (32 weights, always inside one block), looks the
-// codes up in a 16-entry table in LDS, multiplies with x in fp32, folds the
-// block scale into the piece's partial sum, and the row is finished with a
-// wave-level shuffle reduction.
+// 16-bit activations (the decode case) take gemv_4bit_lut_kernel:
+//  * A persistent grid of 16 waves per CU (one 1024-thread workgroup for
+//    M = 1, two of 512 threads otherwise, each with its own 64 KB table);
+//    wave w owns the
+//    contiguous output rows [w N / W, (w + 1) N / W), so every wave streams a
+//    contiguous run of the packed weight.
+//  * A row is cut into slices of 64 lanes x 16 bytes (2048 weights); a lane's
+//    16 bytes are 32 weights inside one block, so one scale per lane-piece.
+//  * Decode: a 64 KB LDS table maps every packed byte to the two code values
+//    as a bf16 (or fp16) pair.  It is replicated 64 times, one copy per lane,
+//    so the lookups of a wave never share a bank; one v_perm_b32 turns a
+//    packed byte and the lane number into the LDS address.
+//  * Multiply: v_dot2_f32_bf16 (v_dot2_f32_f16) multiplies a looked-up pair
+//    with two activations and accumulates in fp32; the block scale is applied
+//    once per 32-weight piece.
+//  * The loads of the next (row group, slice) -- weights, scales and, for
+//    M = 1, the activations -- are issued before the current one is decoded,
+//    and the first ones before the table is built, so HBM latency overlaps
+//    the table setup and the arithmetic.  The table is written as
+//    consecutive 16-byte chunks from kernel-argument values: no global load
+//    and no bank conflict on the way to the barrier.
+//  * Rows finish with a DPP wave reduction.
+// fp32 activations take gemv_4bit_f32x_kernel, a plain fp32 path.
 #include <algorithm>
 
 #include "qmv_launch.hpp"
 
 namespace qmv {
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t uint4v;
+
+constexpr int kLutReplicas = 64;  // one table copy per lane of a wave
+
+// The 16 code values already rounded to the activation type (bf16 or fp16
+// bits), computed on the host.
+struct Table16 {
+  uint32_t h[16];
+};
+
+// Builds the 64 KB code-pair table: entry e = (T[e >> 4], T[e & 15]) as two
+// 16-bit values, 64 copies.  Written as consecutive 16-byte chunks (lane i ->
+// chunk i, so no two lanes of a wave share a bank); the high half of a
+// thread's entries is fixed, the low half is wave-uniform per chunk row and
+// read from the kernel arguments with a scalar index.
+template <int THREADS>
+__device__ __forceinline__ void build_pair_table(uint32_t *lut, const Table16 &table, int tid) {
+  const uint32_t hi_idx = (tid >> 4) & 15;
+  uint32_t hi = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) hi = (hi_idx == (uint32_t)c) ? table.h[c] : hi;
+  hi <<= 16;
+  uint4 *dst = reinterpret_cast<uint4 *>(lut);
+  constexpr int kChunks = 256 * kLutReplicas * 4 / 16;
+#pragma unroll
+  for (int it = 0; it < kChunks / THREADS; ++it) {
+    const int c = it * THREADS + tid;
+    const uint32_t e_hi = __builtin_amdgcn_readfirstlane((uint32_t)c >> 8);  // wave-uniform
+    const uint32_t v = table.h[e_hi] | hi;
+    dst[c] = make_uint4(v, v, v, v);
+  }
+}
+
+template <int XDT>
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+  if constexpr (XDT == kBF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, x), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, x),
+                                  acc, false);
+}
+
+__device__ __forceinline__ void store_y(void *y, int ydt, int64_t i, float v) {
+  if (ydt == kF32) static_cast<float *>(y)[i] = v;
+  else if (ydt == kBF16) static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_bf16_rne(v);
+  else static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_f16_rne(v);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x) {  // rows outside ROW_MASK read 0
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave with DPP moves; the total ends in lane 63
+// and is broadcast from there.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_move<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141, 0xf>(v);  // row_half_mirror
+  v += dpp_move<0x140, 0xf>(v);  // row_mirror: every lane holds its row's sum
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Rows decoded together per step: more rows give more loads in flight, more
+// activation rows more registers per row.
+// M = 1 runs one 1024-thread workgroup per CU (16 waves, <= 128 VGPRs);
+// larger M needs more registers and runs two 512-thread workgroups per CU.
+template <int M>
+struct LutShape {
+  static constexpr int RG = M <= 2 ? 4 : (M <= 4 ? 2 : 1);
+  static constexpr int kThreads = M == 1 ? 1024 : 512;
+  static constexpr int kWgPerCu = M == 1 ? 1 : 2;
+  static constexpr int kMinWavesPerSimd = kThreads / 256;
+  static constexpr bool kPrefetchX = M == 1;  // x pieces travel with the weight loads
+};
+
+template <int M, int XDT, bool DQ>
+__global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSimd) void gemv_4bit_lut_kernel(
+    const uint16_t *__restrict__ x, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
+    int rows_rem) {
+  constexpr int RG = LutShape<M>::RG;
+  constexpr int kGemvThreads = LutShape<M>::kThreads;
+  constexpr bool PX = LutShape<M>::kPrefetchX;
+  constexpr int XW = PX ? 16 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutReplicas];
+  __shared__ float code2[256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform: keeps the per-wave bookkeeping in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kGemvThreads / 64) + (tid >> 6));
+  const int64_t r_begin = (int64_t)wave * rows_per_wave + (wave < rows_rem ? wave : rows_rem);
+  const int64_t r_end = r_begin + rows_per_wave + (wave < rows_rem ? 1 : 0);
+  const int64_t pieces = K >> 5;
+  const int S = (int)((pieces + 63) >> 6);
+  const int64_t ngroups = (r_end - r_begin + RG - 1) / RG;
+  const int64_t half_k = K >> 1;
+
+  struct Buf {
+    uint4 w[RG];
+    float sa[RG];
+    uint32_t sq[RG];
+    uint32_t xs[XW];
+  };
+  auto load_x = [&](int s, uint32_t *xs, int m) {
+    const int64_t pc = (int64_t)s * 64 + lane;
+    uint4 xv[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                   make_uint4(0, 0, 0, 0)};
+    if (pc < pieces) {
+      const uint4 *xp = reinterpret_cast<const uint4 *>(x + m * K + (pc << 5));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[q] = xp[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xs[4 * q] = xv[q].x;
+      xs[4 * q + 1] = xv[q].y;
+      xs[4 * q + 2] = xv[q].z;
+      xs[4 * q + 3] = xv[q].w;
+    }
+  };
+  // issue the loads of (row group g, slice s)
+  auto load = [&](int64_t g, int s, Buf &buf) {
+    const int64_t pc = (int64_t)s * 64 + lane;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int64_t row = r_begin + g * RG + r;
+      buf.w[r] = make_uint4(0, 0, 0, 0);
+      buf.sa[r] = 0.f;
+      buf.sq[r] = 0;
+      if (row < r_end && pc < pieces) {
+        buf.w[r] = *reinterpret_cast<const uint4 *>(packed + row * half_k + (pc << 4));
+        const int64_t b = (row * K + (pc << 5)) >> log2bs;
+        if constexpr (DQ) {
+          buf.sq[r] = sc.q[b];
+          buf.sa[r] = sc.absmax2[b >> sc.log2bs2];
+        } else {
+          buf.sa[r] = sc.absmax[b];
+        }
+      }
+    }
+    if constexpr (PX) load_x(s, buf.xs, 0);
+  };
+
+  Buf b0, b1;
+  if (ngroups > 0) load(0, 0, b0);
+  float offset = 0.f;
+  if constexpr (DQ) {
+    if (tid < 256) code2[tid] = sc.code2[tid];
+    offset = sc.offset[0];
+  }
+  build_pair_table<kGemvThreads>(lut, table, tid);
+  __syncthreads();
+  const uint32_t lane_sel = (uint32_t)lane << 2;
+  const char *lut_bytes = reinterpret_cast<const char *>(lut);
+
+  float acc[RG][M];
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+
+  auto compute = [&](int64_t g, int s, const Buf &buf) {
+    uint32_t xl[PX ? 1 : M][16];
+    if constexpr (!PX) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) load_x(s, xl[m], m);
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const uint32_t w[4] = {buf.w[r].x, buf.w[r].y, buf.w[r].z, buf.w[r].w};
+      uint32_t t[16];
+#pragma unroll
+      for (int bb = 0; bb < 16; ++bb) {
+        const uint32_t addr =
+            __builtin_amdgcn_perm(w[bb >> 2], lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
+        t[bb] = *reinterpret_cast<const uint32_t *>(lut_bytes + addr);
+      }
+      const float ahat = DQ ? code2[buf.sq[r]] * buf.sa[r] + offset : buf.sa[r];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint32_t *xs = PX ? buf.xs : xl[m];
+        float part = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < 16; ++bb) part = dot2<XDT>(t[bb], xs[bb], part);
+        acc[r][m] = fmaf(ahat, part, acc[r][m]);
+      }
+    }
+    if (s == S - 1) {  // the rows of group g are complete
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const int64_t row = r_begin + g * RG + r;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float v = wave_sum(acc[r][m]);
+          acc[r][m] = 0.f;
+          if (lane == r * M + m && row < r_end) store_y(y, ydt, m * N + row, v);
+        }
+      }
+    }
+  };
+
+  // steps (g, s) in order; the loads of the next step go out before the
+  // current one is decoded (two buffers, alternating)
+  int64_t g = 0;
+  int s = 0;
+  while (g < ngroups) {
+    int64_t g1 = g, g2;
+    int s1 = s + 1, s2;
+    if (s1 == S) { s1 = 0; ++g1; }
+    if (g1 < ngroups) load(g1, s1, b1);
+    compute(g, s, b0);
+    if (g1 >= ngroups) break;
+    g2 = g1;
+    s2 = s1 + 1;
+    if (s2 == S) { s2 = 0; ++g2; }
+    if (g2 < ngroups) load(g2, s2, b0);
+    compute(g1, s1, b1);
+    g = g2;
+    s = s2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// M = 1 (the decode step): gemv_4bit_m1_kernel
+//
+// Same table and per-wave row ranges as above, organised for the smallest
+// vector-instruction count per 16-byte piece:
+//  * The work of a wave is a sequence of steps (row group g, slice s); a step
+//    covers RPS rows (1, 2 or 4, unrolled) of one slice.  8 pieces per wave
+//    are always in flight: the loads of step t + 8 / RPS are issued right
+//    after step t is decoded.
+//  * Every load is a buffer load whose resource (base, size) is computed with
+//    scalar instructions per step; the lane's part of the address is a
+//    constant register.  A padding row, a lane past the row's last piece or
+//    (in the prologue of a short wave) a step past the end gets a zero-sized
+//    range: the load returns zeros and moves no data.  In the steady-state
+//    loop every refill is live and unconditional, so the compiler waits for
+//    exactly the step it is about to decode.
+//  * The activation vector is staged once in LDS (when it fits), transposed
+//    so that a slice's 64 lanes read consecutive 16-byte chunks.
+// ---------------------------------------------------------------------------
+constexpr int kM1Threads = 1024;
+constexpr int kM1Slots = 8;          // pieces in flight per wave
+constexpr int kM1XLdsBytes = 90112;  // activations staged in LDS up to K = 45056 (whole slices)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int XDT, bool DQ, int XC, int RPS>  // XC: x chunks staged per thread (0: no staging)
+__global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
+    const uint16_t *__restrict__ x, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
+    int rows_rem) {
+  constexpr bool XLDS = XC > 0;
+  constexpr int D = kM1Slots / RPS;  // steps in flight
+  // one LDS block with the code-pair table at address 0, so a lookup address
+  // needs no base added; then the DQ table and the staged activations
+  __shared__ __attribute__((aligned(16))) uint32_t lds[256 * kLutReplicas + 256 +
+                                                       (XLDS ? kM1XLdsBytes / 4 : 4)];
+  uint32_t *lut = lds;
+  float *code2 = reinterpret_cast<float *>(lds + 256 * kLutReplicas);
+  uint16_t *xl = reinterpret_cast<uint16_t *>(lds + 256 * kLutReplicas + 256);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform: keeps the step bookkeeping in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kM1Threads / 64) + (tid >> 6));
+  const int64_t r_begin = (int64_t)wave * rows_per_wave + (wave < rows_rem ? wave : rows_rem);
+  const int64_t nrows = rows_per_wave + (wave < rows_rem ? 1 : 0);
+  const int64_t pieces = K >> 5;
+  const int S = (int)((pieces + 63) >> 6);
+  const int64_t T = (nrows + RPS - 1) / RPS * S;  // steps of this wave
+  const int64_t half_k = K >> 1;
+  const int bs_shift = log2bs - 5;                // blocks per lane piece: lane >> bs_shift
+  const uint32_t lane_w = (uint32_t)lane << 4;    // byte offset of the lane's piece
+  const uint32_t lane_b = (uint32_t)lane >> bs_shift;  // block offset of the lane's piece
+  const uint32_t blocks_per_slice = 64u >> bs_shift;
+
+  // Prologue loads, oldest first: staged activations, the DQ table, then the
+  // queue.  Loads return in order, so the staging waits only for its own.
+  const int nch = (int)(K >> 3);  // 16-byte chunks of x
+  uint4 xch[XC > 0 ? XC : 1];
+#pragma unroll
+  for (int i = 0; i < XC; ++i) {
+    const int c = i * kM1Threads + tid;
+    xch[i] = reinterpret_cast<const uint4 *>(x)[c < nch ? c : nch - 1];
+  }
+  float c2v = 0.f, offset = 0.f;
+  if constexpr (DQ) {
+    c2v = sc.code2[tid & 255];
+    offset = sc.offset[0];
+  }
+
+  uint4v w[D][RPS];
+  float sa[D][RPS];
+  uint32_t sq[D][RPS];
+  // step cursor (row group g, slice s), wave-uniform
+  struct Step {
+    int64_t g;
+    int s;
+  };
+  auto next = [&](Step &c) {
+    if (++c.s == S) {
+      c.s = 0;
+      ++c.g;
+    }
+  };
+  auto issue = [&](const Step &c, bool step_live, int j) {
+    const int64_t g = c.g;
+    const int s = c.s;
+    const int64_t live_pieces = pieces - (int64_t)s * 64;
+    const uint32_t wbytes = (uint32_t)((live_pieces < 64 ? live_pieces : 64) << 4);
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) {
+      const int64_t rr = g * RPS + r;
+      const bool live = step_live && rr < nrows;
+      const int64_t row = r_begin + (live ? rr : 0);
+      const int64_t e0 = row * K + (int64_t)s * 2048;  // first weight of the row's slice
+      w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(
+          make_rsrc(packed + (e0 >> 1), live ? wbytes : 0u), lane_w, 0, 0);
+      const int64_t ub = e0 >> log2bs;  // first block of the row's slice
+      const uint32_t nbl = live ? blocks_per_slice : 0u;
+      if constexpr (DQ) {
+        sq[j][r] = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(sc.q + ub, nbl), lane_b, 0, 0);
+        const int64_t g0 = ub >> sc.log2bs2;
+        const uint32_t gl = ((uint32_t)(ub & ((1 << sc.log2bs2) - 1)) + lane_b) >> sc.log2bs2;
+        sa[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 make_rsrc(sc.absmax2 + g0, live ? 256u : 0u),
+                                                 gl << 2, 0, 0));
+      } else {
+        sa[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 make_rsrc(sc.absmax + ub, nbl << 2), lane_b << 2,
+                                                 0, 0));
+      }
+    }
+  };
+
+  Step ci = {0, 0};  // next step to issue
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    issue(ci, j < T, j);
+    next(ci);
+  }
+
+  if constexpr (XLDS) {
+    // x as 16-byte chunks, transposed: chunk q (8 values) of piece pc goes to
+    // ((pc / 64) * 4 + q) * 64 + pc % 64
+    // chunks past the end of x, up to whole slices, are zero: a lane past the
+    // row's last piece then multiplies its (zero) codes by zero activations
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = i * kM1Threads + tid;
+      const int pc = c >> 2, q = c & 3;
+      if (c < S * 256)
+        reinterpret_cast<uint4 *>(xl)[(((pc >> 6) << 2) + q) * 64 + (pc & 63)] =
+            c < nch ? xch[i] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  if constexpr (DQ) {
+    if (tid < 256) code2[tid] = c2v;
+  }
+  build_pair_table<kM1Threads>(lut, table, tid);
+  __syncthreads();
+  const uint32_t lane_sel = (uint32_t)lane << 2;
+  const char *lut_bytes = reinterpret_cast<const char *>(lut);
+
+  float acc[RPS];
+#pragma unroll
+  for (int r = 0; r < RPS; ++r) acc[r] = 0.f;
+  uint4v xs[4];
+  int xs_slice = -1;
+
+  auto compute = [&](const Step &c, int j) {
+    const int64_t g = c.g;
+    const int s = c.s;
+    if (s != xs_slice) {  // activations of this slice (wave-uniform)
+      xs_slice = s;
+      if constexpr (XLDS) {
+        const uint4v *xp = reinterpret_cast<const uint4v *>(xl) + s * 256 + lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xs[q] = xp[q * 64];
+      } else {
+        // a lane past the row's last piece multiplies its (zero) codes by
+        // zero activations, so it adds nothing
+        const int64_t pc = (int64_t)s * 64 + lane;
+        const uint4v *xp = reinterpret_cast<const uint4v *>(x + ((pc < pieces ? pc : 0) << 5));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xs[q] = pc < pieces ? xp[q] : uint4v{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) {
+      if (g * RPS + r < nrows) {  // wave-uniform
+        const uint4v wd = w[j][r];
+        float part = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < 16; ++bb) {
+          const uint32_t addr =
+              __builtin_amdgcn_perm(wd[bb >> 2], lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
+          part = dot2<XDT>(*reinterpret_cast<const uint32_t *>(lut_bytes + addr), xs[bb >> 2][bb & 3],
+                           part);
+        }
+        const float ahat = DQ ? code2[sq[j][r]] * sa[j][r] + offset : sa[j][r];
+        acc[r] = fmaf(ahat, part, acc[r]);
+      }
+    }
+    if (s == S - 1) {  // the rows of group g are complete
+#pragma unroll
+      for (int r = 0; r < RPS; ++r) {
+        if (g * RPS + r < nrows) {
+          const float v = wave_sum(acc[r]);
+          if (lane == r) store_y(y, ydt, r_begin + g * RPS + r, v);
+        }
+        acc[r] = 0.f;
+      }
+    }
+  };
+
+  // steady state: every refill is a live step, so the loads are unconditional
+  // and each decode waits for exactly its own step
+  Step cc = {0, 0};  // next step to decode
+  int64_t t0 = 0;
+  for (; t0 + 2 * D <= T; t0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      compute(cc, j);
+      next(cc);
+      issue(ci, true, j);
+      next(ci);
+    }
+  }
+  // drain: fewer than 2 D steps left
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (t0 + j < T) {
+      compute(cc, j);
+      next(cc);
+    }
+    if (t0 + j + D < T) {
+      issue(ci, true, j);
+      next(ci);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (t0 + D + j < T) {
+      compute(cc, j);
+      next(cc);
+    }
+  }
+}
+
+// Plain fp32 path (fp32 activations): a wave per row, fp32 table values and
+// fp32 multiply-adds.
 template <int M, int XDT, int YDT, bool DQ, int QT>
-__global__ __launch_bounds__(256) void gemv_4bit_kernel(const void *__restrict__ xv, int64_t N,
+__global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restrict__ xv, int64_t N,
                                                         int64_t K, const uint8_t *__restrict__ packed,
                                                         Scales sc, int log2bs, void *__restrict__ yv) {
   using XT = typename Storage<XDT>::type;
@@ -70,14 +550,17 @@ __global__ __launch_bounds__(256) void gemv_4bit_kernel(const void *__restrict__
   }
 }
 
-template <int M, int XDT, int YDT>
-static hipError_t launch_gemv_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int M, int YDT>
+static hipError_t launch_f32x_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                                 const Scales &sc, bool dq, int log2bs, int qt, void *y,
                                 hipStream_t st) {
   const unsigned grid = (unsigned)std::min<int64_t>((N + 3) / 4, 1 << 16);
-#define QMV_G(DQV, QTV)                                                                         \
-  hipLaunchKernelGGL((gemv_4bit_kernel<M, XDT, YDT, DQV, QTV>), dim3(grid), dim3(256), 0, st, x, \
-                     N, K, packed, sc, log2bs, y)
+#define QMV_G(DQV, QTV)                                                                       \
+  hipLaunchKernelGGL((gemv_4bit_f32x_kernel<M, kF32, YDT, DQV, QTV>), dim3(grid), dim3(256), 0, \
+                     st, x, N, K, packed, sc, log2bs, y)
   if (dq) {
     if (qt == kNF4) QMV_G(true, kNF4); else QMV_G(true, kFP4);
   } else {
@@ -87,37 +570,139 @@ static hipError_t launch_gemv_m(const void *x, int64_t N, int64_t K, const uint8
   return hipGetLastError();
 }
 
-template <int XDT, int YDT>
-static hipError_t launch_gemv_xy(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
-                                 const Scales &sc, bool dq, int log2bs, int qt, void *y,
-                                 hipStream_t st) {
+template <int YDT>
+static hipError_t launch_f32x(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
+                              const Scales &sc, bool dq, int log2bs, int qt, void *y,
+                              hipStream_t st) {
   switch (M) {
-    case 1: return launch_gemv_m<1, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    case 2: return launch_gemv_m<2, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    case 3: return launch_gemv_m<3, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    case 4: return launch_gemv_m<4, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    case 5: return launch_gemv_m<5, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    case 6: return launch_gemv_m<6, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    case 7: return launch_gemv_m<7, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
-    default: return launch_gemv_m<8, XDT, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
+#define QMV_C(MV) case MV: return launch_f32x_m<MV, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
+    QMV_C(1) QMV_C(2) QMV_C(3) QMV_C(4) QMV_C(5) QMV_C(6) QMV_C(7)
+#undef QMV_C
+    default: return launch_f32x_m<8, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
   }
 }
 
+// fp32 -> bf16 / fp16 bits, round to nearest even, on the host.
+static uint32_t host_bits16(float f, int dt) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (dt == kBF16) return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+static Table16 host_table16(int qt, int dt) {
+  Table16 t;
+  const uint32_t *bits = table_bits(qt);
+  for (int c = 0; c < 16; ++c) t.h[c] = host_bits16(__builtin_bit_cast(float, bits[c]), dt);
+  return t;
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int M, int XDT>
+static hipError_t launch_lut_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
+                               const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
+                               hipStream_t st) {
+  constexpr int kGemvThreads = LutShape<M>::kThreads;
+  const int64_t waves_per_wg = kGemvThreads / 64;
+  int64_t grid = (int64_t)cu_count() * LutShape<M>::kWgPerCu;
+  grid = std::min<int64_t>(grid, (N + waves_per_wg - 1) / waves_per_wg);
+  const int64_t total_waves = grid * waves_per_wg;
+  const int rpw = (int)(N / total_waves), rem = (int)(N % total_waves);
+  const uint16_t *xh = static_cast<const uint16_t *>(x);
+  const Table16 table = host_table16(qt, XDT);
+  if (dq)
+    hipLaunchKernelGGL((gemv_4bit_lut_kernel<M, XDT, true>), dim3((unsigned)grid),
+                       dim3(kGemvThreads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt,
+                       rpw, rem);
+  else
+    hipLaunchKernelGGL((gemv_4bit_lut_kernel<M, XDT, false>), dim3((unsigned)grid),
+                       dim3(kGemvThreads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt,
+                       rpw, rem);
+  return hipGetLastError();
+}
+
 template <int XDT>
-static hipError_t launch_gemv_x(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
-                                const Scales &sc, bool dq, int log2bs, int qt, void *y, int y_dtype,
-                                hipStream_t st) {
-  if (y_dtype == kF32) return launch_gemv_xy<XDT, kF32>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
-  if (y_dtype == kF16) return launch_gemv_xy<XDT, kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
-  return launch_gemv_xy<XDT, kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
+static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *packed,
+                            const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
+                            hipStream_t st) {
+  const int64_t waves_per_wg = kM1Threads / 64;
+  int64_t grid = (int64_t)cu_count();
+  grid = std::min<int64_t>(grid, (N + waves_per_wg - 1) / waves_per_wg);
+  const int64_t total_waves = grid * waves_per_wg;
+  const int rpw = (int)(N / total_waves), rem = (int)(N % total_waves);
+  const uint16_t *xh = static_cast<const uint16_t *>(x);
+  const Table16 table = host_table16(qt, XDT);
+  // x staged in LDS as K / 8 chunks of 16 bytes, XC per thread
+  // (whole slices of 2048 values; the tail of the last one is zero-filled)
+  const int64_t slices = (K + 2047) / 2048;
+  const int64_t need = (slices * 256 + kM1Threads - 1) / kM1Threads;
+  const int xc =
+      slices * 4096 > kM1XLdsBytes ? 0 : (need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 6);
+  // rows decoded together: as many as a wave has, up to 4
+  const double avg_rows = (double)N / (double)total_waves;
+  const int rps = avg_rows >= 3.0 ? 4 : (avg_rows >= 1.5 ? 2 : 1);
+#define QMV_M1(DQV, XCV, RV)                                                                   \
+  hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, RV>), dim3((unsigned)grid),          \
+                     dim3(kM1Threads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt, rpw, \
+                     rem)
+#define QMV_M1R(DQV, XCV)                                          \
+  switch (rps) {                                                   \
+    case 4: QMV_M1(DQV, XCV, 4); break;                            \
+    case 2: QMV_M1(DQV, XCV, 2); break;                            \
+    default: QMV_M1(DQV, XCV, 1); break;                           \
+  }
+#define QMV_M1X(DQV)                        \
+  switch (xc) {                             \
+    case 0: QMV_M1R(DQV, 0); break;         \
+    case 1: QMV_M1R(DQV, 1); break;         \
+    case 2: QMV_M1R(DQV, 2); break;         \
+    case 4: QMV_M1R(DQV, 4); break;         \
+    default: QMV_M1R(DQV, 6); break;        \
+  }
+  if (dq) {
+    QMV_M1X(true);
+  } else {
+    QMV_M1X(false);
+  }
+#undef QMV_M1R
+#undef QMV_M1X
+#undef QMV_M1
+  return hipGetLastError();
+}
+
+template <int XDT>
+static hipError_t launch_lut(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
+                             const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
+                             hipStream_t st) {
+  if (M == 1) return launch_m1<XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, st);
+  switch (M) {
+#define QMV_C(MV) case MV: return launch_lut_m<MV, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, st);
+    QMV_C(1) QMV_C(2) QMV_C(3) QMV_C(4) QMV_C(5) QMV_C(6) QMV_C(7)
+#undef QMV_C
+    default: return launch_lut_m<8, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, st);
+  }
 }
 
 hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_t K,
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
                             void *y, int y_dtype, hipStream_t st) {
-  if (x_dtype == kF32) return launch_gemv_x<kF32>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
-  if (x_dtype == kF16) return launch_gemv_x<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
-  return launch_gemv_x<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
+  if (x_dtype == kBF16) return launch_lut<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
+  if (x_dtype == kF16) return launch_lut<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
+  if (y_dtype == kF32) return launch_f32x<kF32>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
+  if (y_dtype == kF16) return launch_f32x<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
+  return launch_f32x<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
 }
 
 }  // namespace qmv
