@@ -7,12 +7,15 @@
 // bit-exact: the nearest-code decision is made against exact thresholds, and
 // every float operation is an explicitly rounded one.
 #include <algorithm>
+#include <type_traits>
 
 #include "qmv_launch.hpp"
 
 #pragma clang fp contract(off)
 
 namespace qmv {
+
+static int device_cus();
 
 int log2_exact(int64_t v) {
   int l = 0;
@@ -66,58 +69,84 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
 // A workgroup of 256 threads takes a tile of 256 * E consecutive elements;
 // each thread owns E of them (one 16- or 32-byte load), so G = blocksize / E
 // neighbouring threads share a block.  The block absmax is reduced across
-// those G threads (wave shuffles, then LDS when a block spans waves).  For
-// each block the fp32 thresholds are derived from the exact float64 products
-// absmax * mid[j]:
-//   mid > 0: x moves up past the threshold only when x > absmax * mid
-//            (a tie stays with the smaller magnitude), and for fp32 x that is
+// those G threads (wave shuffles, then LDS when a block spans waves).
+//
+// Exact thresholds.  For each block the fp32 thresholds are derived from the
+// exact float64 products absmax * mid[j] (mid: midpoints of adjacent distinct
+// code values):
+//   mid > 0: x moves up past the threshold only when x > absmax * mid (a tie
+//            stays with the smaller magnitude); for fp32 x that is
 //            x > RD(absmax * mid);
 //   mid < 0: x moves up when x >= absmax * mid, i.e. x > pred(RU(absmax * mid)).
-// The code is the number of thresholds x exceeds, mapped to the table's code.
+// The code is the number of thresholds x exceeds (its rank), mapped to the
+// table's code.  The G threads of a block compute its thresholds together
+// and leave them in LDS as [-inf, t_0, ..., t_last, +inf].
+//
+// Rank.  n = x / absmax is approximated in fp32 and rounded into one of 32
+// bins of width 1/16 on [-1, 1]; a small table gives the rank at the bin's
+// centre.  Adjacent thresholds are more than 1/16 apart (in n), so the true
+// rank differs from that candidate c by at most one, and two exact
+// comparisons settle it: rank = c + [x > t_c] - [x <= t_(c-1)].
 // ---------------------------------------------------------------------------
+struct QuantArgs {
+  Midpoints4 mids;
+  uint8_t cand[32];  // rank at the centre of bin b: n = -1 + (b + 0.5) / 16
+};
+
 template <int DT, int QT, int E>
 __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restrict__ Wv,
                                                             int64_t numel, int log2bs,
-                                                            Midpoints4 mids,
+                                                            QuantArgs qa,
                                                             uint8_t *__restrict__ packed,
                                                             float *__restrict__ absmax) {
   using T = typename Storage<DT>::type;
+  constexpr int NT = QT == kNF4 ? 15 : 14;  // thresholds (FP4's +0 and -0 are one value)
+  constexpr int TS = 17;                    // LDS floats per block: sentinels + thresholds
   const T *W = static_cast<const T *>(Wv);
   __shared__ float wave_max[4];
+  __shared__ float thr[256 * E / 32 * TS];  // up to tile / 32 blocks per tile
+  __shared__ uint32_t cand[32];
+  __shared__ double mids[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int G = (1 << log2bs) / E;  // threads per block: 4 .. 256
+  const int G = (1 << log2bs) / E;  // threads per block: 2 .. 256
+  const int j_in_blk = tid & (G - 1);
+  const int blk_in_tile = tid / G;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
+  if (tid < 32) cand[tid] = qa.cand[tid];
+  if (tid < NT) mids[tid] = qa.mids.mid[tid];
+  __syncthreads();
 
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t e0 = t * tile + (int64_t)tid * E;
-    float v[E];
-    if (e0 + E <= numel) {
-      if constexpr (DT == kF32) {
+  // full tiles' loads: E elements per thread, 16- or 32-byte vector loads
+  auto load_full = [&](int64_t tt, float (&v)[E]) {
+    const int64_t e0 = tt * tile + (int64_t)tid * E;
+    if constexpr (DT == kF32) {
 #pragma unroll
-        for (int i = 0; i < E; i += 4) {
-          const float4 q = *reinterpret_cast<const float4 *>(W + e0 + i);
-          v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < E; i += 8) {
-          const uint4 q = *reinterpret_cast<const uint4 *>(W + e0 + i);
-          const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[i + 2 * j] = bits16_to_f32<DT>(w[j] & 0xffffu);
-            v[i + 2 * j + 1] = bits16_to_f32<DT>(w[j] >> 16);
-          }
-        }
+      for (int i = 0; i < E; i += 4) {
+        const float4 q = *reinterpret_cast<const float4 *>(W + e0 + i);
+        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = (e0 + i < numel) ? load_elem<DT>(W, e0 + i) : 0.f;
+      for (int i = 0; i < E; i += 8) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(W + e0 + i);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[i + 2 * j] = bits16_to_f32<DT>(w[j] & 0xffffu);
+          v[i + 2 * j + 1] = bits16_to_f32<DT>(w[j] >> 16);
+        }
+      }
     }
+  };
 
+  // FULL: a whole tile, whose stores are all unconditional (every lane of a
+  // block writes the same absmax), so the load waits can be counted exactly
+  auto process = [&](int64_t t, const float (&v)[E], auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int64_t e0 = t * tile + (int64_t)tid * E;
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -131,28 +160,39 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       float mm = wave_max[w0];
       for (int i = 1; i < wpb; ++i) mm = fmaxf(mm, wave_max[w0 + i]);
       m = mm;
-      __syncthreads();
     }
-    if ((tid & (G - 1)) == 0 && e0 < numel) absmax[e0 >> log2bs] = m;
+    if (FULL || (j_in_blk == 0 && e0 < numel)) absmax[e0 >> log2bs] = m;
 
-    // NF4 has 16 distinct values (15 thresholds); FP4's +0 and -0 coincide (14)
-    constexpr int NT = QT == kNF4 ? 15 : 14;
-    float th[NT];
+    // this block's thresholds, shared out among its G threads
+    float *bt = thr + blk_in_tile * TS;
     const double ad = (double)m;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const double p = ad * mids.mid[j];  // exact
-      th[j] = mids.mid[j] > 0.0 ? f64_to_f32_rd(p)
-                                : __uint_as_float(f32_step_down_bits(f64_to_f32_ru(p)));
+    for (int j = j_in_blk; j < NT; j += G) {
+      const double mid = mids[j];
+      const double p = ad * mid;  // exact
+      bt[1 + j] = mid > 0.0 ? f64_to_f32_rd(p)
+                            : __uint_as_float(f32_step_down_bits(f64_to_f32_ru(p)));
     }
+    if (j_in_blk == 0) {
+      bt[0] = -INFINITY;
+      bt[NT + 1] = INFINITY;
+    }
+    __syncthreads();
 
+    // approximate n = x / absmax: tiny blocks are scaled up by 2^100 (exact)
+    // so the reciprocal stays finite, huge ones down by 2^100 so it stays
+    // normal (only the candidate uses n); an all-zero block has n = 0
+    const float sc = m < 0x1p-100f ? 0x1p100f : (m > 0x1p100f ? 0x1p-100f : 1.f);
+    const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m * sc) : 0.f;
     uint32_t code[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      int r = 0;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) r += (v[i] > th[j]) ? 1 : 0;
-      code[i] = (e0 + i < numel) ? rank_to_code<QT>(r) : 0u;
+      const float n = (v[i] * sc) * inv;
+      int bin = (int)fmaf(n, 16.f, 16.f);
+      bin = bin < 0 ? 0 : (bin > 31 ? 31 : bin);
+      const int c = (int)cand[bin];
+      const float lo = bt[c], hi = bt[c + 1];  // t_(c-1), t_c
+      const int r = c + (v[i] > hi ? 1 : 0) - (v[i] <= lo ? 1 : 0);
+      code[i] = (FULL || e0 + i < numel) ? rank_to_code<QT>(r) : 0u;
     }
 
     uint32_t word[E / 8];
@@ -165,7 +205,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       word[w] = x;
     }
     uint8_t *dst = packed + (e0 >> 1);
-    if (e0 + E <= numel) {
+    if (FULL || e0 + E <= numel) {
       if constexpr (E == 8) {
         *reinterpret_cast<uint32_t *>(dst) = word[0];
       } else {
@@ -176,29 +216,65 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       for (int b = 0; b < E / 2; ++b)
         if (e0 + 2 * b < numel) dst[b] = (uint8_t)(word[b >> 2] >> (8 * (b & 3)));
     }
+    __syncthreads();  // thr and wave_max are reused by the next tile
+  };
+
+  // full tiles: the next tile's loads are issued before this one is processed
+  // (unconditionally, clamped to the last full tile, so the waits are exact)
+  const int64_t nfull = numel / tile;
+  int64_t t = blockIdx.x;
+  if (nfull > 0) {
+    float nx[E];
+    load_full(t < nfull ? t : nfull - 1, nx);
+    for (; t < nfull; t += gridDim.x) {
+      float v[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = nx[i];
+      const int64_t tn = t + gridDim.x;
+      load_full(tn < nfull ? tn : nfull - 1, nx);
+      process(t, v, std::true_type{});
+    }
+  }
+  // the ragged last tile, if any (same workgroup stride, so exactly one takes it)
+  if (t < ntiles) {
+    const int64_t e0 = t * tile + (int64_t)tid * E;
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (e0 + i < numel) ? load_elem<DT>(W, e0 + i) : 0.f;
+    process(t, v, std::false_type{});
   }
 }
 
 template <int DT, int QT>
-static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, const Midpoints4 &m,
+static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, const QuantArgs &qa,
                                     uint8_t *packed, float *absmax, hipStream_t st) {
   const int E = log2bs > 11 ? 16 : 8;  // a tile always holds whole blocks
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
-  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 20);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, 8 * device_cus()));
   if (E == 8)
     hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, 8>), dim3(grid), dim3(256), 0, st, W, numel,
-                       log2bs, m, packed, absmax);
+                       log2bs, qa, packed, absmax);
   else
     hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, 16>), dim3(grid), dim3(256), 0, st, W, numel,
-                       log2bs, m, packed, absmax);
+                       log2bs, qa, packed, absmax);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int log2bs, int qt,
                                 const Midpoints4 &m, uint8_t *packed, float *absmax,
                                 hipStream_t st) {
-#define QMV_Q(DT, QT) return launch_quantize_t<DT, QT>(W, numel, log2bs, m, packed, absmax, st)
+  // candidate rank at each bin centre, from the exact midpoints
+  QuantArgs qa{};
+  qa.mids = m;
+  const int nt = qt == kNF4 ? 15 : 14;
+  for (int b = 0; b < 32; ++b) {
+    const double centre = -1.0 + (b + 0.5) / 16.0;
+    int c = 0;
+    for (int j = 0; j < nt; ++j) c += m.mid[j] < centre ? 1 : 0;
+    qa.cand[b] = (uint8_t)c;
+  }
+#define QMV_Q(DT, QT) return launch_quantize_t<DT, QT>(W, numel, log2bs, qa, packed, absmax, st)
   if (qt == kNF4) {
     if (w_dtype == kF32) QMV_Q(kF32, kNF4);
     if (w_dtype == kF16) QMV_Q(kF16, kNF4);
@@ -225,31 +301,59 @@ hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int l
 // ---------------------------------------------------------------------------
 constexpr int kFanIn = 256;
 
+// One workgroup sums 16 consecutive runs: the runs are staged in LDS with
+// coalesced loads (rows padded to 257 doubles so that the 16 summing threads
+// hit different banks), then thread r adds run r in order.  The level that
+// produces a single value also writes offset = fp32(S / n).
+constexpr int kSumRuns = 16;
+
 template <typename In>
 __global__ __launch_bounds__(256) void dq_sum_kernel(const In *__restrict__ in, int64_t n,
-                                                     double *__restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+                                                     double *__restrict__ out, int64_t n_total,
+                                                     float *__restrict__ offset) {
+  __shared__ double stage[kSumRuns * (kFanIn + 1)];
+  const int tid = threadIdx.x;
   const int64_t nout = (n + kFanIn - 1) / kFanIn;
-  if (i >= nout) return;
-  const int64_t s0 = i * kFanIn;
-  const int64_t s1 = s0 + kFanIn < n ? s0 + kFanIn : n;
-  double s = 0.0;
-  for (int64_t k = s0; k < s1; ++k) s = __dadd_rn(s, (double)in[k]);
-  out[i] = s;
+  const int64_t run0 = (int64_t)blockIdx.x * kSumRuns;
+  const int64_t base = run0 * kFanIn;
+#pragma unroll
+  for (int i = 0; i < kSumRuns; ++i) {  // element base + i * 256 + tid
+    const int64_t e = base + (int64_t)i * kFanIn + tid;
+    stage[i * (kFanIn + 1) + tid] = e < n ? (double)in[e] : 0.0;
+  }
+  __syncthreads();
+  if (tid < kSumRuns && run0 + tid < nout) {
+    const int64_t r = run0 + tid;
+    const int len = (int)((n - r * kFanIn) < kFanIn ? (n - r * kFanIn) : kFanIn);
+    const double *row = stage + tid * (kFanIn + 1);
+    double s = 0.0;
+    // in order, 32 values at a time: the reads of a chunk are independent of
+    // the additions, so they are in flight together
+    for (int k0 = 0; k0 < len; k0 += 32) {
+      double v[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) v[k] = row[k0 + k];  // zero past len (staged as 0)
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        if (k0 + k < len) s = __dadd_rn(s, v[k]);
+    }
+    out[r] = s;
+    if (nout == 1) offset[0] = (float)__ddiv_rn(s, (double)n_total);
+  }
 }
 
-__global__ void dq_offset_kernel(const double *__restrict__ S, int64_t n, float *__restrict__ offset) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) offset[0] = (float)__ddiv_rn(S[0], (double)n);
-}
-
-template <int E>  // scales per thread: blocksize2 / min(blocksize2, 256)
+// Encode: a workgroup takes a tile of 256 * E consecutive scales, E per
+// thread (E = 8, or 16 when a group of 4096 would span more than 256
+// threads); the G = blocksize2 / E threads of a group reduce max |c|, then
+// every thread runs E binary searches side by side (their LDS reads overlap).
+template <int E>
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict__ absmax,
                                                         int64_t n, int log2bs2, Code2Table code2,
                                                         const float *__restrict__ offset,
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ absmax2,
                                                         float *__restrict__ code2_out) {
-  __shared__ double mid[255];
+  __shared__ double mid[256];
   __shared__ float wave_max[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -258,23 +362,18 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
   if (blockIdx.x == 0) code2_out[tid] = code2.v[tid];
   __syncthreads();
 
-  const int bs2 = 1 << log2bs2;
-  const int G = bs2 / E;  // threads per group: 32 .. 256
+  const int G = (1 << log2bs2) / E;  // threads per group: 2 .. 256
   const int64_t tile = (int64_t)256 * E;
   const int64_t ntiles = (n + tile - 1) / tile;
   const float off = offset[0];
 
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    // thread tid owns scales i0, i0 + G, ... of its group (strided, coalesced)
-    const int g_in_tile = tid / G;
-    const int j = tid % G;
-    const int64_t gbase = t * tile + (int64_t)g_in_tile * bs2;
+    const int64_t i0 = t * tile + (int64_t)tid * E;
     float c[E];
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int64_t i = gbase + j + (int64_t)e * G;
-      c[e] = (i < n) ? __fsub_rn(absmax[i], off) : 0.f;
+      c[e] = (i0 + e < n) ? __fsub_rn(absmax[i0 + e], off) : 0.f;
       m = fmaxf(m, fabsf(c[e]));
     }
     const int gw = G < 64 ? G : 64;
@@ -289,23 +388,27 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
       m = mm;
       __syncthreads();
     }
-    if (j == 0 && gbase < n) absmax2[gbase >> log2bs2] = m;
+    if ((tid & (G - 1)) == 0 && i0 < n) absmax2[i0 >> log2bs2] = m;
     const double sd = (double)m;
+    int lo[E], hi[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t i = gbase + j + (int64_t)e * G;
-      if (i >= n) continue;
-      const double x = (double)c[e];
-      int lo = 0, hi = 255;
-      while (lo < hi) {
-        const int md = (lo + hi) >> 1;
+    for (int e = 0; e < E; ++e) { lo[e] = 0; hi[e] = 255; }
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {  // 255 thresholds: 8 halvings
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int md = (lo[e] + hi[e]) >> 1;
         const double mj = mid[md];
         const double thr = sd * mj;  // exact
+        const double x = (double)c[e];
         const bool up = mj > 0.0 ? (x > thr) : (x >= thr);
-        if (up) lo = md + 1; else hi = md;
+        lo[e] = up ? md + 1 : lo[e];
+        hi[e] = up ? hi[e] : md;
       }
-      q[i] = (uint8_t)lo;
     }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (i0 + e < n) q[i0 + e] = (uint8_t)lo[e];
   }
 }
 
@@ -322,39 +425,32 @@ size_t double_quant_workspace_bytes(int64_t nblocks) {
 hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,
                                const Code2Table &code2, uint8_t *q, float *absmax2, float *offset,
                                float *code2_out, double *ws, hipStream_t st) {
-  // summation tree
+  // summation tree: level 1 over the scales, then over the partial sums
   int64_t n = nblocks;
   double *level = ws;
   int64_t nout = (n + kFanIn - 1) / kFanIn;
-  hipLaunchKernelGGL(dq_sum_kernel<float>, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st,
-                     absmax, n, level);
+  hipLaunchKernelGGL(dq_sum_kernel<float>, dim3((unsigned)((nout + kSumRuns - 1) / kSumRuns)),
+                     dim3(256), 0, st, absmax, n, level, nblocks, offset);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   while (nout > 1) {
     double *next = level + nout;
     const int64_t n2 = (nout + kFanIn - 1) / kFanIn;
-    hipLaunchKernelGGL(dq_sum_kernel<double>, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st,
-                       level, nout, next);
+    hipLaunchKernelGGL(dq_sum_kernel<double>, dim3((unsigned)((n2 + kSumRuns - 1) / kSumRuns)),
+                       dim3(256), 0, st, level, nout, next, nblocks, offset);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     level = next;
     nout = n2;
   }
-  hipLaunchKernelGGL(dq_offset_kernel, dim3(1), dim3(64), 0, st, level, nblocks, offset);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int bs2 = 1 << log2bs2;
-  const int64_t tile = bs2 > 256 ? bs2 : 256;
+  const int E = bs2 > 2048 ? 16 : 8;
+  const int64_t tile = 256 * (int64_t)E;
   const int64_t ntiles = (nblocks + tile - 1) / tile;
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
 #define QMV_E(EV)                                                                          \
   hipLaunchKernelGGL(dq_encode_kernel<EV>, dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
                      code2, offset, q, absmax2, code2_out)
-  switch (bs2 <= 256 ? 1 : bs2 / 256) {
-    case 1: QMV_E(1); break;
-    case 2: QMV_E(2); break;
-    case 4: QMV_E(4); break;
-    case 8: QMV_E(8); break;
-    default: QMV_E(16); break;
-  }
+  if (E == 8) QMV_E(8); else QMV_E(16);
 #undef QMV_E
   return hipGetLastError();
 }
@@ -382,38 +478,82 @@ hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t n, float 
 // ---------------------------------------------------------------------------
 // dequantize_4bit
 //
-// One thread per 16 packed bytes (32 elements, always inside one block since
-// blocksize >= 32 and chunks are 32-aligned): one 16-byte load, the block
-// scale, 32 explicitly rounded fp32 products from a 16-entry table in LDS,
-// then RNE to the output type and 16-byte stores.  A ragged tail is handled
-// element by element by the thread that owns the last chunk.
+// A thread handles 16-byte pieces (32 elements, always inside one block since
+// blocksize >= 32 and pieces are 32-aligned), U of them at a time with every
+// load issued before the first is used.  Each packed byte indexes a 256-entry
+// LDS table of fp32 code pairs; the two products with the block scale are
+// rounded once to fp32 and then converted (bf16: v_cvt_pk_bf16_f32, round to
+// nearest even, two elements per instruction).  Loads past the last full
+// piece are clamped to it (they are never stored), so the compiler can count
+// them; a ragged tail is written element by element by one thread.
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v_t;
+
+template <int ODT>
+__device__ __forceinline__ uint32_t cvt_pair(float lo, float hi) {
+  if constexpr (ODT == kBF16) {
+    const f32x2_t v = {materialize(lo), materialize(hi)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+  } else {
+    return f32_to_f16_rne(lo) | (f32_to_f16_rne(hi) << 16);
+  }
+}
+
+constexpr int kDeqThreads = 256;
+constexpr int kDeqU = 4;
+
 template <int QT, int ODT, bool DQ>
-__global__ __launch_bounds__(256) void dequantize_4bit_kernel(const uint8_t *__restrict__ packed,
-                                                              Scales sc, int64_t numel,
-                                                              int log2bs, void *__restrict__ outv) {
+__global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
+    const uint8_t *__restrict__ packed, Scales sc, int64_t numel, int log2bs, void *__restrict__ outv) {
   using OT = typename Storage<ODT>::type;
   OT *out = static_cast<OT *>(outv);
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = __uint_as_float(table_bits(QT)[threadIdx.x]);
+  __shared__ float2 lut2[256];  // byte -> (T[byte >> 4], T[byte & 15])
+  __shared__ float code2[256];
+  const int tid = threadIdx.x;
+  {
+    const uint32_t *tb = table_bits(QT);
+    lut2[tid] = make_float2(__uint_as_float(tb[tid >> 4]), __uint_as_float(tb[tid & 15]));
+    if constexpr (DQ) code2[tid] = sc.code2[tid];
+  }
+  const float offset = DQ ? sc.offset[0] : 0.f;
   __syncthreads();
-  const int64_t nfull = numel >> 5;
-  const int64_t nchunks = (numel + 31) >> 5;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
-       c += (int64_t)gridDim.x * 256) {
-    const float a = block_scale<DQ>(sc, (c << 5) >> log2bs);
-    if (c < nfull) {
-      const uint4 p = *reinterpret_cast<const uint4 *>(packed + (c << 4));
-      const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+
+  const int64_t nfull = numel >> 5;  // whole 16-byte pieces
+  const int64_t stride = (int64_t)gridDim.x * kDeqThreads;
+  for (int64_t base = (int64_t)blockIdx.x * kDeqThreads + tid; base < nfull; base += stride * kDeqU) {
+    uint4 p[kDeqU];
+    float sa[kDeqU];
+    uint32_t sq[kDeqU];
+#pragma unroll
+    for (int u = 0; u < kDeqU; ++u) {
+      const int64_t c0 = base + u * stride;
+      const int64_t c = c0 < nfull ? c0 : nfull - 1;
+      p[u] = *reinterpret_cast<const uint4 *>(packed + (c << 4));
+      const int64_t b = (c << 5) >> log2bs;
+      if constexpr (DQ) {
+        sq[u] = sc.q[b];
+        sa[u] = sc.absmax2[b >> sc.log2bs2];
+      } else {
+        sa[u] = sc.absmax[b];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDeqU; ++u) {
+      const int64_t c = base + u * stride;
+      if (c >= nfull) break;
+      const float a = DQ ? code2[sq[u]] * sa[u] + offset : sa[u];
+      const uint32_t pw[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
       if constexpr (ODT == kF32) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           float o[8];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = (pw[w] >> (8 * b)) & 0xffu;
-            o[2 * b] = lut[byte >> 4] * a;
-            o[2 * b + 1] = lut[byte & 15u] * a;
+          for (int bb = 0; bb < 4; ++bb) {
+            const float2 t = lut2[(pw[w] >> (8 * bb)) & 0xffu];
+            o[2 * bb] = t.x * a;
+            o[2 * bb + 1] = t.y * a;
           }
           float4 *dst = reinterpret_cast<float4 *>(out + (c << 5) + 8 * w);
           dst[0] = make_float4(o[0], o[1], o[2], o[3]);
@@ -424,36 +564,53 @@ __global__ __launch_bounds__(256) void dequantize_4bit_kernel(const uint8_t *__r
         for (int w = 0; w < 4; ++w) {
           uint32_t o[4];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = (pw[w] >> (8 * b)) & 0xffu;
-            const uint32_t h0 = f32_to_bits16<ODT>(lut[byte >> 4] * a);
-            const uint32_t h1 = f32_to_bits16<ODT>(lut[byte & 15u] * a);
-            o[b] = h0 | (h1 << 16);
+          for (int bb = 0; bb < 4; ++bb) {
+            const float2 t = lut2[(pw[w] >> (8 * bb)) & 0xffu];
+            o[bb] = cvt_pair<ODT>(t.x * a, t.y * a);
           }
           *reinterpret_cast<uint4 *>(out + (c << 5) + 8 * w) = make_uint4(o[0], o[1], o[2], o[3]);
         }
       }
-    } else {
-      for (int64_t e = c << 5; e < numel; ++e) {
-        const uint32_t byte = packed[e >> 1];
-        const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);
-        store_elem<ODT>(out, e, lut[code] * a);
-      }
     }
   }
+  // ragged tail: elements [32 * nfull, numel), by one thread
+  if (blockIdx.x == 0 && tid == 0 && (numel & 31)) {
+    const int64_t e0 = nfull << 5;
+    const float a = block_scale<DQ>(sc, e0 >> log2bs);
+    for (int64_t e = e0; e < numel; ++e) {
+      const uint32_t byte = packed[e >> 1];
+      const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);
+      const float2 t = lut2[code << 4];  // (T[code], T[0])
+      store_elem<ODT>(out, e, t.x * a);
+    }
+  }
+}
+
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int QT, int ODT>
 static hipError_t launch_dequant_t(const uint8_t *packed, const Scales &sc, bool dq, int64_t numel,
                                    int log2bs, void *out, hipStream_t st) {
-  const int64_t nchunks = (numel + 31) >> 5;
-  const unsigned grid = (unsigned)std::min<int64_t>((nchunks + 255) / 256, 1 << 16);
+  const int64_t nfull = numel >> 5;
+  const int64_t want = (nfull + (int64_t)kDeqThreads * kDeqU - 1) / ((int64_t)kDeqThreads * kDeqU);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 8 * device_cus()));
   if (dq)
-    hipLaunchKernelGGL((dequantize_4bit_kernel<QT, ODT, true>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((dequantize_4bit_kernel<QT, ODT, true>), dim3(grid), dim3(kDeqThreads), 0, st,
                        packed, sc, numel, log2bs, out);
   else
-    hipLaunchKernelGGL((dequantize_4bit_kernel<QT, ODT, false>), dim3(grid), dim3(256), 0, st,
-                       packed, sc, numel, log2bs, out);
+    hipLaunchKernelGGL((dequantize_4bit_kernel<QT, ODT, false>), dim3(grid), dim3(kDeqThreads), 0,
+                       st, packed, sc, numel, log2bs, out);
   return hipGetLastError();
 }
 
