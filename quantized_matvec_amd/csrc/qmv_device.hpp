@@ -59,6 +59,8 @@ __device__ __forceinline__ float block_scale(const Scales &s, int64_t b) {
   }
 }
 
+__device__ __forceinline__ float sc_offset(const Scales &s) { return s.offset[0]; }
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }

@@ -2,12 +2,13 @@
 // ("Feat/mps gemm 4bit bf16", table "What runs natively now": gemm_4bit).
 //
 // The pages' design dequantizes into a scratch buffer and then runs a GEMM.
-// Here the weight never leaves the chip in bf16: each 128 x 32 weight tile is
-// read packed (16 bytes per row), dequantized by VALU into an LDS tile, and
+// Here the weight never leaves the chip in bf16: each 128 x 64 weight tile is
+// read packed (32 bytes per row), dequantized by VALU into an LDS tile, and
 // consumed by bf16 matrix-core instructions (v_mfma_f32_32x32x16_bf16) with
 // fp32 accumulation.  A 256-thread workgroup computes a 128 x 128 C tile as
 // 2 x 2 waves of 64 x 64.
 #include <algorithm>
+#include <type_traits>
 
 #include "qmv_launch.hpp"
 
@@ -15,29 +16,113 @@ namespace qmv {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kLds = kBK + 8;  // padded LDS row, in bf16 elements (80 bytes)
+// Tile: 128 (M) x 128 (N) x 64 (K); 4 waves as 2 x 2, each 64 x 64 as 2 x 2
+// accumulators of v_mfma_f32_32x32x16_bf16.  LDS rows are padded to 72 bf16
+// (144 bytes) so that the 32 rows an operand read touches fall in different
+// banks.  Two LDS stages: while the matrix cores consume stage k, the global
+// loads of tile k + 1 are in flight, and they are dequantized into the other
+// stage afterwards (one barrier per k-tile).
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLd = kBK + 8;                    // padded row, bf16 elements
+constexpr int kStage = (kBM + kBN) * kLd;       // bf16 elements per stage
 
-template <int CDT, bool DQ, int QT>
-__global__ __launch_bounds__(256) void gemm_4bit_kernel(const uint16_t *__restrict__ A, int64_t M,
-                                                        int64_t N, int64_t K,
-                                                        const uint8_t *__restrict__ packed,
-                                                        Scales sc, int log2bs,
-                                                        void *__restrict__ Cv) {
+struct Table16f {
+  float v[16];
+};
+
+template <int CDT, bool DQ>
+__global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__restrict__ A, int64_t M,
+                                                           int64_t N, int64_t K,
+                                                           const uint8_t *__restrict__ packed,
+                                                           Scales sc, int log2bs, Table16f table,
+                                                           void *__restrict__ Cv) {
   using CT = typename Storage<CDT>::type;
   CT *C = static_cast<CT *>(Cv);
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLds];
-  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+  __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
+  __shared__ float code2[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  if (tid < 16) lut[tid] = __uint_as_float(table_bits(QT)[tid]);
-
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t KT = (K + kBK - 1) / kBK;
+  const bool k_tail = (K % kBK) != 0;  // last tile has 32 of 64 columns
+
+  // loader roles: thread t moves row t / 2, columns [32 (t % 2), +32) of the
+  // A tile and of the weight tile
+  const int lr = tid >> 1, lh = tid & 1;
+  const int64_t arow = m0 + lr < M ? m0 + lr : M - 1;  // rows past M are never stored
+  const int64_t brow = n0 + lr < N ? n0 + lr : N - 1;  // columns past N likewise
+  // two register sets: tile k + 2 is loaded while tile k is multiplied and
+  // tile k + 1 (loaded an iteration earlier) is staged
+  uint4 ra_[2][4];
+  uint4 rb_[2];
+  float rsa_[2];
+  uint32_t rsq_[2];
+  auto load_tile = [&](int64_t kt, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+    uint4(&ra)[4] = ra_[SL];
+    uint4 &rb = rb_[SL];
+    float &rsa = rsa_[SL];
+    uint32_t &rsq = rsq_[SL];
+    int64_t k = kt * kBK + 32 * lh;
+    if (k >= K) k = K - 32;  // the missing half of a tail tile (zeroed when staged)
+    const uint4 *ap = reinterpret_cast<const uint4 *>(A + arow * K + k);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra[q] = ap[q];
+    const int64_t e0 = brow * K + k;
+    rb = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
+    const int64_t b = e0 >> log2bs;
+    if constexpr (DQ) {
+      rsq = sc.q[b];
+      rsa = sc.absmax2[b >> sc.log2bs2];
+    } else {
+      rsa = sc.absmax[b];
+    }
+  };
+  auto stage_tile = [&](int64_t kt, int buf, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+    const uint4(&ra)[4] = ra_[SL];
+    const uint4 &rb = rb_[SL];
+    const float rsa = rsa_[SL];
+    const uint32_t rsq = rsq_[SL];
+    (void)rsq;
+    uint16_t *As = smem + buf * kStage;
+    uint16_t *Bs = As + kBM * kLd;
+    const bool zero = k_tail && kt == KT - 1 && lh == 1;
+    uint4 *ad = reinterpret_cast<uint4 *>(As + lr * kLd + 32 * lh);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ad[q] = zero ? make_uint4(0, 0, 0, 0) : ra[q];
+    const float a = zero ? 0.f : (DQ ? code2[rsq] * rsa + sc_offset(sc) : rsa);
+    const uint32_t pw[4] = {rb.x, rb.y, rb.z, rb.w};
+    uint32_t o[16];
+#pragma unroll
+    for (int bb = 0; bb < 16; ++bb) {
+      const float2 t = lut2[(pw[bb >> 2] >> (8 * (bb & 3))) & 0xffu];
+      // dequantized weights: fp32(T * a_hat) rounded to bf16 (nearest even)
+      const f32x2_t v = {materialize(t.x * a), materialize(t.y * a)};
+      o[bb] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
+    uint4 *bd = reinterpret_cast<uint4 *>(Bs + lr * kLd + 32 * lh);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load_tile(0, S0{});
+  load_tile(KT > 1 ? 1 : 0, S1{});
+  lut2[tid] = make_float2(table.v[tid >> 4], table.v[tid & 15]);
+  if constexpr (DQ) code2[tid] = sc.code2[tid];
+  __syncthreads();
+  stage_tile(0, 0, S0{});
+  __syncthreads();
+
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -45,66 +130,47 @@ __global__ __launch_bounds__(256) void gemm_4bit_kernel(const uint16_t *__restri
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  __syncthreads();
 
-  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    {  // A tile: 128 rows x 64 bytes, two 16-byte pieces per thread
-      const int r = tid >> 1, h = tid & 1;
-      const int64_t gm = m0 + r;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-      if (gm < M) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(A + gm * K + k0 + h * 16);
-        v0 = src[0];
-        v1 = src[1];
-      }
-      *reinterpret_cast<uint4 *>(&As[r * kLds + h * 16]) = v0;
-      *reinterpret_cast<uint4 *>(&As[r * kLds + h * 16 + 8]) = v1;
-    }
-    if (tid < kBN) {  // B tile: one packed 16-byte row piece per thread -> 32 bf16
-      const int64_t gn = n0 + tid;
-      uint32_t o[16];
-#pragma unroll
-      for (int b = 0; b < 16; ++b) o[b] = 0;
-      if (gn < N) {
-        const int64_t e0 = gn * K + k0;
-        const float a = block_scale<DQ>(sc, e0 >> log2bs);
-        const uint4 p = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
-        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-        for (int b = 0; b < 16; ++b) {
-          const uint32_t byte = (pw[b >> 2] >> (8 * (b & 3))) & 0xffu;
-          const uint32_t h0 = f32_to_bf16_rne(lut[byte >> 4] * a);
-          const uint32_t h1 = f32_to_bf16_rne(lut[byte & 15u] * a);
-          o[b] = h0 | (h1 << 16);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint4 *>(&Bs[tid * kLds + 8 * q]) =
-            make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-    }
-    __syncthreads();
+  auto mma_tile = [&](int buf) {
+    const uint16_t *As = smem + buf * kStage;
+    const uint16_t *Bs = As + kBM * kLd;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t a[2], b[2];
+      bf16x8_t af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm * 64 + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8_t *>(&As[row * kLds + ks * 16 + (lane >> 5) * 8]);
+        af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * kLd + ks * 16 + (lane >> 5) * 8);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = wn * 64 + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const bf16x8_t *>(&Bs[col * kLds + ks * 16 + (lane >> 5) * 8]);
+        bfr[j] = *reinterpret_cast<const bf16x8_t *>(Bs + col * kLd + ks * 16 + (lane >> 5) * 8);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  // tile kt sits in LDS stage kt % 2 and tile kt + 1 in register set (kt + 1) % 2;
+  // each step loads tile kt + 2 into the register set tile kt used
+  // (loads past the end re-read the last tile, so they are unconditional)
+  auto clampk = [&](int64_t k) { return k < KT ? k : KT - 1; };
+  int64_t kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    load_tile(clampk(kt + 2), S0{});
+    mma_tile(0);
+    stage_tile(kt + 1, 1, S1{});
+    __syncthreads();
+    load_tile(clampk(kt + 3), S1{});
+    mma_tile(1);
+    if (kt + 2 < KT) stage_tile(kt + 2, 0, S0{});
     __syncthreads();
   }
+  if (kt < KT) mma_tile(0);  // odd tile count: the last tile is in stage 0
 
   // 32 x 32 accumulator layout: column = lane % 32,
   // row = 8 * (r / 4) + 4 * (lane / 32) + r % 4 for accumulator register r.
@@ -127,18 +193,18 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
                             hipStream_t st) {
   const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   const uint16_t *a = static_cast<const uint16_t *>(A);
-#define QMV_M(CDT, DQV, QTV)                                                                    \
-  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV, QTV>), grid, dim3(256), 0, st, a, M, N, K, \
-                     packed, sc, log2bs, C)
-#define QMV_MQ(CDT, DQV) \
-  if (qt == kNF4) QMV_M(CDT, DQV, kNF4); else QMV_M(CDT, DQV, kFP4)
+  Table16f table;
+  const uint32_t *bits = table_bits(qt);
+  for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
+#define QMV_M(CDT, DQV)                                                                        \
+  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV>), grid, dim3(256), 0, st, a, M, N, K, packed, \
+                     sc, log2bs, table, C)
 #define QMV_MD(CDT) \
-  if (dq) { QMV_MQ(CDT, true); } else { QMV_MQ(CDT, false); }
+  if (dq) { QMV_M(CDT, true); } else { QMV_M(CDT, false); }
   if (c_dtype == kF32) { QMV_MD(kF32); }
   else if (c_dtype == kF16) { QMV_MD(kF16); }
   else { QMV_MD(kBF16); }
 #undef QMV_MD
-#undef QMV_MQ
 #undef QMV_M
   return hipGetLastError();
 }
