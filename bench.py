@@ -55,21 +55,30 @@ def source_hash(paths):
     return h.hexdigest()
 
 
-GEMV_SOURCES = ["quantized_matvec_amd/csrc/qmv_gemv.hip", "quantized_matvec_amd/csrc/qmv_device.hpp"]
+GEMV_SOURCES = ["quantized_matvec_amd/csrc/qmv_gemv.hip", "quantized_matvec_amd/csrc/qmv_device.hpp",
+                "quantized_matvec_amd/csrc/qmv_launch.hpp"]
 
 
 def measured_traffic():
-    """HBM bytes per gemv launch from the committed rocprofv3 counter summary,
-    or None when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "gemv_4bit_nf4_14336x4096_m1_traffic.json")
+    """HBM bytes per gemv launch from the committed rocprofv3 counter summary
+    (lines "key: value"), or None when the kernel source changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemv_4bit_nf4_14336x4096_m1_traffic.txt")
+    d = {}
     try:
         with open(path) as f:
-            d = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                k, sep, v = line.partition(":")
+                if sep and k.strip() and not k.startswith(("#", " ")):
+                    d[k.strip()] = v.strip()
+    except OSError:
         return None
     if d.get("kernel_source_sha256") != source_hash(GEMV_SOURCES):
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return int(float(d["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def timed_loop(fn, iters, stream, torch):
@@ -83,9 +92,13 @@ def timed_loop(fn, iters, stream, torch):
     return start.elapsed_time(end) / iters * 1e3   # microseconds per call
 
 
-def cpu_baseline(W_cpu, x_cpu, budget_s=12.0):
-    """The oracle's gemv (scale reconstruction, dequantize, float64 matmul) on
-    a bounded sample of output rows, single-threaded."""
+def cpu_baseline(W_cpu, x_cpu, budget_s=15.0, rows=256):
+    """The oracle's gemv on a bounded sample: the first `rows` output rows of
+    the weight, single-threaded.  Untimed set-up: block scales of the whole
+    weight (the double-quant mean needs all of them), double quant, and the
+    oracle quantize of the sampled rows.  Timed, repeated until `budget_s`:
+    scale reconstruction of the sampled blocks, dequantization and the float64
+    matmul.  Bytes are counted per output row exactly as for the GPU kernel."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -93,28 +106,44 @@ def cpu_baseline(W_cpu, x_cpu, budget_s=12.0):
     import oracle as O
     W64 = W_cpu.to(torch.float64).numpy()
     x64 = x_cpu.to(torch.float64).numpy()
-    # the double-quant state needs every block scale of the weight
-    absmax = O.block_absmax(W64, BS).astype(np.float32)
-    q, a2, off = O.double_quant(absmax, BS2)
-    rows_done, t_used, chunk = 0, 0.0, 64
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s and rows_done + chunk <= N:
-            r = np.arange(rows_done, rows_done + chunk)
-            packed, _ = O.quantize_4bit(W64[r], BS, "nf4")      # codes of these rows (untimed)
-            nb0 = rows_done * K // BS
-            blocks = np.arange(nb0, nb0 + chunk * K // BS)
-            ts = time.perf_counter()
-            # scale reconstruction of these rows' blocks (their groups may straddle the chunk)
-            ahat = (O.linear8_table()[q[blocks]] * a2[blocks // BS2] + off).astype(np.float32)
-            O.matmul_4bit(x64, packed, ahat, chunk, K, BS, "nf4")
-            t_used += time.perf_counter() - ts
-            rows_done += chunk
-    per_row = (K // 2 + K // BS * (1 + 4 / BS2)) + 2      # packed + scales + y per row
-    gbs = rows_done * per_row / t_used / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} of {N} output rows of the gemv (dequantize + float64 matmul), "
-                      f"{t_used:.1f} s of single-threaded CPU time; same bytes-per-row accounting"}
+        absmax = O.block_absmax(W64, BS).astype(np.float32)
+        q, a2, off = O.double_quant(absmax, BS2)
+        packed, _ = O.quantize_4bit(W64[:rows], BS, "nf4")
+        nbs = rows * K // BS
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            ahat = O.dequant_absmax(q[:nbs], a2[:-(-nbs // BS2)], off, None, BS2)
+            O.matmul_4bit(x64, packed, ahat, rows, K, BS, "nf4")
+            passes += 1
+            t = time.perf_counter() - t0
+            if t >= budget_s:
+                break
+    per_row = K // 2 + K // BS * (1 + 4 / BS2) + 2 * M_GEMV      # packed + DQ scales + y
+    gbs = passes * rows * per_row / t / 1e9
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle gemv (DQ scale decode + dequantize + float64 matmul) over the first "
+                      f"{rows} of {N} output rows, {passes} passes in {t:.1f} s on one thread; "
+                      f"bytes per row counted as for the GPU kernel"}
+
+
+COPY_BYTES = 1 << 30
+
+
+def counters_run(name, fns, n_copies, dev, torch):
+    """A short program for rocprofv3 counter passes: a plain 1 GiB device copy
+    (its FETCH_SIZE / WRITE_SIZE per byte calibrate the counters), then ten
+    launches of one kernel, each on a different weight copy."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy of {COPY_BYTES} bytes done", flush=True)
+    for i in range(10):
+        fns[name](i % n_copies)
+    torch.cuda.synchronize()
+    print(f"10 launches of {name} done", flush=True)
 
 
 def main():
@@ -124,6 +153,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", choices=["gemv_4bit", "gemm_4bit", "dequantize_4bit", "quantize_4bit"],
+                    help="for hardware-counter runs: one 1 GiB copy (the calibration kernel), "
+                         "then 10 launches of the named kernel over distinct weight copies")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -168,6 +200,15 @@ def main():
             qmv.dequantize_4bit(p, st, out=wout[i % n_w])
             qmv.gemv_4bit(x, p, st, out=y)
             qmv.gemm_4bit(A, p, st, out=C)
+
+        if args.counters:
+            counters_run(args.counters, dict(gemv_4bit=lambda i: qmv.gemv_4bit(x, packs[i], states[i], out=y),
+                                             gemm_4bit=lambda i: qmv.gemm_4bit(A, packs[i], states[i], out=C),
+                                             dequantize_4bit=lambda i: qmv.dequantize_4bit(
+                                                 packs[i], states[i], out=wout[i % n_w]),
+                                             quantize_4bit=lambda i: qmv.quantize_4bit(
+                                                 Ws[i % n_w], BS, "nf4")), n_p, dev, torch)
+            return
 
         for i in range(args.warmup):
             step(i)
@@ -246,7 +287,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "LLM MLP up-projection 14336x4096 bf16 (0.1% x20 outliers), NF4 block 64, "
                                "double-quantized scales (256-groups); gemv M=1, gemm M=512",
