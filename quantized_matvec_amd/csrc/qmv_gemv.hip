@@ -267,9 +267,9 @@ __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSim
 // Same table and per-wave row ranges as above, organised for the smallest
 // vector-instruction count per 16-byte piece:
 //  * The work of a wave is a sequence of steps (row group g, slice s); a step
-//    covers RPS rows (1, 2 or 4, unrolled) of one slice.  8 pieces per wave
-//    are always in flight: the loads of step t + 8 / RPS are issued right
-//    after step t is decoded.
+//    covers RPS rows (1, 2 or 4, unrolled) of one slice.  D steps per wave
+//    are in flight: the loads of step t + D are issued right after step t is
+//    decoded.
 //  * Every load is a buffer load whose resource (base, size) is computed with
 //    scalar instructions per step; the lane's part of the address is a
 //    constant register.  A padding row, a lane past the row's last piece or
@@ -281,7 +281,13 @@ __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSim
 //    so that a slice's 64 lanes read consecutive 16-byte chunks.
 // ---------------------------------------------------------------------------
 constexpr int kM1Threads = 1024;
-constexpr int kM1Slots = 8;          // pieces in flight per wave
+// Steps in flight per wave, by rows per step: 4 pieces (4 KB) per wave for
+// RPS = 4 and 2, 2 pieces for RPS = 1.  With 16 waves per CU this keeps about
+// 32-64 KB of weight loads outstanding per CU; deeper queues stall the
+// issuing waves (the memory pipeline is full) while loaded data waits to be
+// decoded, and measured slower on every layer shape.
+template <int RPS>
+constexpr int m1_depth() { return RPS == 4 ? 1 : 2; }
 constexpr int kM1XLdsBytes = 90112;  // activations staged in LDS up to K = 45056 (whole slices)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
     Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
     int rows_rem) {
   constexpr bool XLDS = XC > 0;
-  constexpr int D = kM1Slots / RPS;  // steps in flight
+  constexpr int D = m1_depth<RPS>();  // steps in flight
   // one LDS block with the code-pair table at address 0, so a lookup address
   // needs no base added; then the DQ table and the staged activations
   __shared__ __attribute__((aligned(16))) uint32_t lds[256 * kLutReplicas + 256 +
