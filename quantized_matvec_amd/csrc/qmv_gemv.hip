@@ -322,7 +322,8 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
   const int bs_shift = log2bs - 5;                // blocks per lane piece: lane >> bs_shift
   const uint32_t lane_w = (uint32_t)lane << 4;    // byte offset of the lane's piece
   const uint32_t lane_b = (uint32_t)lane >> bs_shift;  // block offset of the lane's piece
-  const uint32_t blocks_per_slice = 64u >> bs_shift;
+  // blocks a slice touches (one when a block is longer than a slice)
+  const uint32_t blocks_per_slice = bs_shift > 6 ? 1u : 64u >> bs_shift;
 
   // Prologue loads, oldest first: staged activations, the DQ table, then the
   // queue.  Loads return in order, so the staging waits only for its own.

@@ -115,6 +115,36 @@ def test_gemv_dtypes(xd, yd):
     assert rel_l2(f64(y), ref) <= tol
 
 
+@pytest.mark.parametrize("bs", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("dq", [False, True])
+def test_matmul_all_blocksizes(bs, dq):
+    """Every block size, including blocks longer than the 2048-weight slices
+    the M = 1 kernels stream; K = 4096 + bs leaves a partial last slice."""
+    N, K = 300, 4096 + bs
+    W = gaussian((N, K), 0.02, bs + dq, "bf16")
+    x = gaussian((5, K), 1.0, bs + 7, "bf16")
+    p_ref, ahat = oracle_state(f64(W), bs, "nf4", dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "nf4", double_quant=dq)
+    for M, f in ((1, qmv.gemv_4bit), (3, qmv.gemv_4bit), (5, qmv.gemm_4bit)):
+        ref = O.matmul_4bit(f64(x[:M]), p_ref, ahat, N, K, bs, "nf4")
+        y = f(x[:M].contiguous().cuda(), packed, st, out_dtype=torch.float32)
+        assert rel_l2(f64(y), ref) <= 1e-2, (M, bs, dq)
+
+
+def test_gemv_m1_long_rows():
+    """K = 49152: the activations are too long to stage in LDS, so the M = 1
+    kernel reads them from global memory per slice."""
+    N, K = 70, 49152
+    W = gaussian((N, K), 0.02, 77, "bf16")
+    x = gaussian((1, K), 1.0, 78, "bf16")
+    for dq in (False, True):
+        p_ref, ahat = oracle_state(f64(W), 64, "nf4", dq)
+        packed, st = qmv.quantize_4bit(W.cuda(), 64, "nf4", double_quant=dq)
+        y = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
+        ref = O.matmul_4bit(f64(x), p_ref, ahat, N, K, 64, "nf4")
+        assert rel_l2(f64(y), ref) <= 1e-2
+
+
 def test_gemv_minimal_shapes():
     for N, K in ((1, 32), (5, 64), (64, 96)):
         W = gaussian((N, K), 0.02, N, "bf16")
