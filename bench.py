@@ -17,6 +17,7 @@ HIP events on the launch stream while rotating over distinct weight copies
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -220,20 +221,27 @@ def main():
 
         kiters = args.kernel_iters
         kern = {}
+        # per-kernel loops call the C ABI directly with prepared arguments,
+        # so the host keeps ahead of kernels of a few microseconds
+        L = qmv.lib()
+        s_h = stream.cuda_stream
+        structs = [st._c() for st in states]          # kept alive for the byref handles
+        scs = [ctypes.byref(c) for c in structs]
+        p_ptr = [p.data_ptr() for p in packs]
+        x_ptr, y_ptr, A_ptr, C_ptr = x.data_ptr(), y.data_ptr(), A.data_ptr(), C.data_ptr()
+        w_ptr = [w.data_ptr() for w in wout]
 
         def run_gemv(i):
-            qmv.gemv_4bit(x, packs[i % n_p], states[i % n_p], out=y)
+            L.qmv_gemv_4bit(x_ptr, 2, M_GEMV, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, y_ptr, 2, s_h)
 
         def run_gemm(i):
-            qmv.gemm_4bit(A, packs[i % n_p], states[i % n_p], out=C)
+            L.qmv_gemm_4bit(A_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, C_ptr, 2, s_h)
 
         def run_deq(i):
-            qmv.dequantize_4bit(packs[i % n_p], states[i % n_p], out=wout[i % n_w])
+            L.qmv_dequantize_4bit(p_ptr[i % n_p], scs[i % n_p], N * K, BS, 0, w_ptr[i % n_w], 2, s_h)
 
         qbuf = [torch.empty_like(packed0) for _ in range(n_w)]
         abuf = [torch.empty_like(st0.absmax_q, dtype=torch.float32) for _ in range(n_w)]
-        L = qmv.lib()
-        s_h = stream.cuda_stream
 
         def run_quant(i):      # the raw entry point (no allocation inside the loop)
             L.qmv_quantize_4bit(Ws[i % n_w].data_ptr(), 2, N * K, BS, 0, qbuf[i % n_w].data_ptr(),
@@ -242,7 +250,7 @@ def main():
         dq_out = [(torch.empty_like(st0.absmax_q), torch.empty_like(st0.absmax2),
                    torch.empty_like(st0.offset), torch.empty_like(st0.code2)) for _ in range(n_w)]
         nbk = N * K // BS
-        ws = torch.empty(L.qmv_double_quant_workspace(nbk), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(L.qmv_double_quant_workspace(nbk), dtype=torch.uint8, device=dev)
 
         def run_dq(i):
             q, a2, off, c2 = dq_out[i % n_w]

@@ -87,7 +87,8 @@ typedef struct {
 int qmv_quantize_4bit(const void *W, qmv_dtype w_dtype, int64_t numel, int32_t blocksize,
                       qmv_quant_type quant_type, uint8_t *packed, float *absmax, void *stream);
 
-/* Bytes of device workspace qmv_double_quant needs for ``nblocks`` scales. */
+/* Bytes of device workspace qmv_double_quant needs for ``nblocks`` scales
+ * (the partial sums of the mean). */
 size_t qmv_double_quant_workspace(int64_t nblocks);
 
 /*
@@ -105,7 +106,9 @@ size_t qmv_double_quant_workspace(int64_t nblocks);
  *   offset      [1] device out: fp32(S / nblocks), S the float64 sum of the
  *               scales taken in a fixed tree (sequential runs of 256, repeated)
  *   code2_out   [256] device out: the table used, for the decode side
- *   workspace   device scratch of at least qmv_double_quant_workspace(nblocks) bytes
+ *   workspace   device scratch of at least qmv_double_quant_workspace(nblocks)
+ *               bytes (any contents); calls that share a workspace must not
+ *               overlap.
  */
 int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
                      const float *code2_host, uint8_t *absmax_q, float *absmax2, float *offset,

@@ -128,6 +128,20 @@ size_t qmv_double_quant_workspace(int64_t nblocks) {
   return nblocks > 0 ? double_quant_workspace_bytes(nblocks) : 0;
 }
 
+// A second-level table is usable when it is finite and strictly increasing
+// and every midpoint of neighbours is nonzero and exact with <= 29
+// significant bits (so the encoder's float64 thresholds are exact).
+static int check_code2(const Code2Table &t) {
+  for (int k = 0; k < 256; ++k)
+    if (!isfinite(t.v[k])) return QMV_ERR_INVALID_ARG;
+  for (int k = 0; k + 1 < 256; ++k) {
+    if (!(t.v[k] < t.v[k + 1])) return QMV_ERR_UNSUPPORTED;  // strictly increasing
+    const double m = exact_midpoint((double)t.v[k], (double)t.v[k + 1]);
+    if (isnan(m) || m == 0.0 || sig_bits(m) > 29) return QMV_ERR_UNSUPPORTED;
+  }
+  return QMV_OK;
+}
+
 int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
                      const float *code2_host, uint8_t *absmax_q, float *absmax2, float *offset,
                      float *code2_out, void *workspace, size_t workspace_bytes, void *stream) {
@@ -139,22 +153,23 @@ int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
   if (!aligned16(absmax) || !aligned16(absmax_q) || !aligned16(absmax2) || !aligned16(offset) ||
       !aligned16(code2_out) || !aligned16(workspace))
     return QMV_ERR_ALIGNMENT;
-  Code2Table t{};
+  // the default table is checked once; a caller's table on every call
+  static const Code2Table kDefault = [] {
+    Code2Table d{};
+    qmv_default_code2(d.v);
+    return d;
+  }();
+  static const int kDefaultStatus = check_code2(kDefault);
+  Code2Table t = kDefault;
+  bool linear = true;
   if (code2_host) {
     memcpy(t.v, code2_host, sizeof(t.v));
-  } else {
-    qmv_default_code2(t.v);
+    linear = memcmp(t.v, kDefault.v, sizeof(t.v)) == 0;
   }
-  for (int k = 0; k < 256; ++k)
-    if (!isfinite(t.v[k])) return QMV_ERR_INVALID_ARG;
-  for (int k = 0; k + 1 < 256; ++k) {
-    if (!(t.v[k] < t.v[k + 1])) return QMV_ERR_UNSUPPORTED;  // strictly increasing
-    const double m = exact_midpoint((double)t.v[k], (double)t.v[k + 1]);
-    if (isnan(m) || m == 0.0 || sig_bits(m) > 29) return QMV_ERR_UNSUPPORTED;
-  }
-  return launch_status(launch_double_quant(absmax, nblocks, log2_exact(blocksize2), t, absmax_q,
-                                           absmax2, offset, code2_out,
-                                           static_cast<double *>(workspace),
+  const int rc = linear ? kDefaultStatus : check_code2(t);
+  if (rc != QMV_OK) return rc;
+  return launch_status(launch_double_quant(absmax, nblocks, log2_exact(blocksize2), t, linear,
+                                           absmax_q, absmax2, offset, code2_out, workspace,
                                            (hipStream_t)stream));
 }
 

@@ -119,24 +119,28 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   if (tid < NT) mids[tid] = qa.mids.mid[tid];
   __syncthreads();
 
-  // full tiles' loads: E elements per thread, 16- or 32-byte vector loads
-  auto load_full = [&](int64_t tt, float (&v)[E]) {
+  // full tiles' loads: E elements per thread as raw 16-byte words (E / 4
+  // for fp32, E / 8 for 16-bit types); they are converted only when the tile
+  // is processed, so a prefetched tile is not waited for at its load
+  constexpr int NW = DT == kF32 ? E / 4 : E / 8;
+  auto load_full = [&](int64_t tt, uint4 (&raw)[NW]) {
     const int64_t e0 = tt * tile + (int64_t)tid * E;
-    if constexpr (DT == kF32) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(W + e0);
 #pragma unroll
-      for (int i = 0; i < E; i += 4) {
-        const float4 q = *reinterpret_cast<const float4 *>(W + e0 + i);
-        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
-      }
-    } else {
+    for (int i = 0; i < NW; ++i) raw[i] = src[i];
+  };
+  auto convert = [&](const uint4 (&raw)[NW], float (&v)[E]) {
 #pragma unroll
-      for (int i = 0; i < E; i += 8) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(W + e0 + i);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      if constexpr (DT == kF32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(w[j]);
+      } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[i + 2 * j] = bits16_to_f32<DT>(w[j] & 0xffffu);
-          v[i + 2 * j + 1] = bits16_to_f32<DT>(w[j] >> 16);
+          v[8 * i + 2 * j] = bits16_to_f32<DT>(w[j] & 0xffffu);
+          v[8 * i + 2 * j + 1] = bits16_to_f32<DT>(w[j] >> 16);
         }
       }
     }
@@ -224,12 +228,11 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   const int64_t nfull = numel / tile;
   int64_t t = blockIdx.x;
   if (nfull > 0) {
-    float nx[E];
+    uint4 nx[NW];
     load_full(t < nfull ? t : nfull - 1, nx);
     for (; t < nfull; t += gridDim.x) {
       float v[E];
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = nx[i];
+      convert(nx, v);
       const int64_t tn = t + gridDim.x;
       load_full(tn < nfull ? tn : nfull - 1, nx);
       process(t, v, std::true_type{});
@@ -293,62 +296,96 @@ hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int l
 // 1. The mean of the scales: float64 sums over consecutive runs of 256 in a
 //    fixed order, level after level, until one value S is left; offset =
 //    fp32(S / nblocks).  The order is part of the contract, so every run is a
-//    plain sequential loop in one thread.
+//    plain sequential loop in one thread.  Every workgroup of the first
+//    launch sums 16 runs of the first level; one workgroup then sums the
+//    remaining (few) levels and writes the offset.
 // 2. Per group of blocksize2 scales: c = fp32(a - offset), s = max |c|, and
 //    the code of c / s is the rank of c among the exact float64 thresholds
-//    s * mid[j] of the (strictly increasing) 256-entry table, found by binary
-//    search; ties go toward zero as in quantize_4bit.
+//    s * mid[j] of the (strictly increasing) 256-entry table; ties go toward
+//    zero as in quantize_4bit.  For the default linear table the rank is
+//    within one of round(127 c / s) + 127 and two threshold compares settle
+//    it; any other table takes a binary search.
 // ---------------------------------------------------------------------------
 constexpr int kFanIn = 256;
+constexpr int kSumRuns = 16;              // runs per workgroup pass
 
-// One workgroup sums 16 consecutive runs: the runs are staged in LDS with
-// coalesced loads (rows padded to 257 doubles so that the 16 summing threads
-// hit different banks), then thread r adds run r in order.  The level that
-// produces a single value also writes offset = fp32(S / n).
-constexpr int kSumRuns = 16;
-
+// Sums runs [16 g, 16 g + 16) of `in` (n values): the runs are staged in LDS
+// (rows padded to 257 doubles so that the 16 summing threads hit different
+// banks) with all loads in flight together; thread r then adds run r in
+// order.  Values past n load as zero, and adding +0 leaves the (non-negative)
+// sum unchanged, so a short last run needs no length test.
 template <typename In>
-__global__ __launch_bounds__(256) void dq_sum_kernel(const In *__restrict__ in, int64_t n,
-                                                     double *__restrict__ out, int64_t n_total,
-                                                     float *__restrict__ offset) {
-  __shared__ double stage[kSumRuns * (kFanIn + 1)];
+__device__ __forceinline__ void sum_runs16(const In *__restrict__ in, int64_t n, int64_t g,
+                                           double *__restrict__ out, double *stage) {
   const int tid = threadIdx.x;
   const int64_t nout = (n + kFanIn - 1) / kFanIn;
-  const int64_t run0 = (int64_t)blockIdx.x * kSumRuns;
+  const int64_t run0 = g * kSumRuns;
   const int64_t base = run0 * kFanIn;
+  const int64_t rem = n - base;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(in + base, (uint32_t)((rem < kSumRuns * kFanIn ? rem : kSumRuns * kFanIn) * sizeof(In)));
+  In v[kSumRuns];
 #pragma unroll
   for (int i = 0; i < kSumRuns; ++i) {  // element base + i * 256 + tid
-    const int64_t e = base + (int64_t)i * kFanIn + tid;
-    stage[i * (kFanIn + 1) + tid] = e < n ? (double)in[e] : 0.0;
+    const uint32_t off = (uint32_t)((i * kFanIn + tid) * sizeof(In));
+    if constexpr (sizeof(In) == 4)
+      v[i] = __builtin_bit_cast(In, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    else
+      v[i] = __builtin_bit_cast(In, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
   }
+#pragma unroll
+  for (int i = 0; i < kSumRuns; ++i) stage[i * (kFanIn + 1) + tid] = (double)v[i];
   __syncthreads();
   if (tid < kSumRuns && run0 + tid < nout) {
-    const int64_t r = run0 + tid;
-    const int len = (int)((n - r * kFanIn) < kFanIn ? (n - r * kFanIn) : kFanIn);
     const double *row = stage + tid * (kFanIn + 1);
     double s = 0.0;
-    // in order, 32 values at a time: the reads of a chunk are independent of
-    // the additions, so they are in flight together
-    for (int k0 = 0; k0 < len; k0 += 32) {
-      double v[32];
+    // 32 values at a time: the reads of a chunk are independent of the
+    // additions, so they are in flight together
+    for (int k0 = 0; k0 < kFanIn; k0 += 32) {
+      double w[32];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) v[k] = row[k0 + k];  // zero past len (staged as 0)
+      for (int k = 0; k < 32; ++k) w[k] = row[k0 + k];
 #pragma unroll
-      for (int k = 0; k < 32; ++k)
-        if (k0 + k < len) s = __dadd_rn(s, v[k]);
+      for (int k = 0; k < 32; ++k) s = __dadd_rn(s, w[k]);
     }
-    out[r] = s;
-    if (nout == 1) offset[0] = (float)__ddiv_rn(s, (double)n_total);
+    out[run0 + tid] = s;
   }
+  __syncthreads();  // stage is reused
+}
+
+// First level: workgroup g sums runs [16 g, 16 g + 16) of the scales.  When
+// that level is already a single run it also writes the offset.
+__global__ __launch_bounds__(256) void dq_sum_kernel(const float *__restrict__ absmax, int64_t n,
+                                                     double *__restrict__ levels,
+                                                     float *__restrict__ offset) {
+  __shared__ double stage[kSumRuns * (kFanIn + 1)];
+  sum_runs16<float>(absmax, n, blockIdx.x, levels, stage);
+  if (n <= kFanIn && threadIdx.x == 0) offset[0] = (float)__ddiv_rn(levels[0], (double)n);
+}
+
+// The remaining levels, in one workgroup (a kernel boundary separates it from
+// the first level, so no cross-workgroup hand-off is needed), then the offset.
+__global__ __launch_bounds__(256) void dq_top_kernel(double *__restrict__ levels, int64_t nl,
+                                                     int64_t n, float *__restrict__ offset) {
+  __shared__ double stage[kSumRuns * (kFanIn + 1)];
+  double *level = levels;
+  while (nl > 1) {
+    double *next = level + nl;
+    const int64_t nn = (nl + kFanIn - 1) / kFanIn;
+    for (int64_t g = 0; g * kSumRuns < nn; ++g) sum_runs16<double>(level, nl, g, next, stage);
+    level = next;
+    nl = nn;
+  }
+  if (threadIdx.x == 0) offset[0] = (float)__ddiv_rn(level[0], (double)n);  // written by thread 0
 }
 
 // Encode: a workgroup takes a tile of 256 * E consecutive scales, E per
 // thread (E = 8, or 16 when a group of 4096 would span more than 256
-// threads); the G = blocksize2 / E threads of a group reduce max |c|, then
-// every thread runs E binary searches side by side (their LDS reads overlap).
+// threads); the G = blocksize2 / E threads of a group reduce max |c|.
 template <int E>
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict__ absmax,
                                                         int64_t n, int log2bs2, Code2Table code2,
+                                                        int linear,
                                                         const float *__restrict__ offset,
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ absmax2,
@@ -369,11 +406,20 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
 
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t i0 = t * tile + (int64_t)tid * E;
+    // the tile's scales through a range-limited buffer: no branch per load
+    const int64_t rem = n - t * tile;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(absmax + t * tile, (uint32_t)((rem < tile ? rem : tile) * 4));
+    float a[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, (uint32_t)((tid * E + e) * 4), 0, 0));
     float c[E];
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      c[e] = (i0 + e < n) ? __fsub_rn(absmax[i0 + e], off) : 0.f;
+      c[e] = (i0 + e < n) ? __fsub_rn(a[e], off) : 0.f;
       m = fmaxf(m, fabsf(c[e]));
     }
     const int gw = G < 64 ? G : 64;
@@ -390,25 +436,44 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
     }
     if ((tid & (G - 1)) == 0 && i0 < n) absmax2[i0 >> log2bs2] = m;
     const double sd = (double)m;
-    int lo[E], hi[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) { lo[e] = 0; hi[e] = 255; }
-#pragma unroll
-    for (int step = 0; step < 8; ++step) {  // 255 thresholds: 8 halvings
+    // c above the threshold of midpoint j (ties toward zero)
+    auto above = [&](double x, int j) {
+      const double mj = mid[j];
+      const double thr = sd * mj;  // exact
+      return mj > 0.0 ? (x > thr) : (x >= thr);
+    };
+    int code[E];
+    if (linear) {
+      const float inv = m > 0.f ? 127.f / m : 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int md = (lo[e] + hi[e]) >> 1;
-        const double mj = mid[md];
-        const double thr = sd * mj;  // exact
+        int k = (int)rintf(c[e] * inv) + 127;
+        k = k < 0 ? 0 : (k > 254 ? 254 : k);  // code 255 (> 1) is never nearest
         const double x = (double)c[e];
-        const bool up = mj > 0.0 ? (x > thr) : (x >= thr);
-        lo[e] = up ? md + 1 : lo[e];
-        hi[e] = up ? hi[e] : md;
+        k += (k < 255 && above(x, k)) ? 1 : 0;
+        k -= (k > 0 && !above(x, k - 1)) ? 1 : 0;
+        code[e] = k;
       }
+    } else {
+      int lo[E], hi[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) { lo[e] = 0; hi[e] = 255; }
+#pragma unroll
+      for (int step = 0; step < 8; ++step) {  // 255 thresholds: 8 halvings
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int md = (lo[e] + hi[e]) >> 1;
+          const bool up = above((double)c[e], md);
+          lo[e] = up ? md + 1 : lo[e];
+          hi[e] = up ? hi[e] : md;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) code[e] = lo[e];
     }
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (i0 + e < n) q[i0 + e] = (uint8_t)lo[e];
+      if (i0 + e < n) q[i0 + e] = (uint8_t)code[e];
   }
 }
 
@@ -423,24 +488,17 @@ size_t double_quant_workspace_bytes(int64_t nblocks) {
 }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,
-                               const Code2Table &code2, uint8_t *q, float *absmax2, float *offset,
-                               float *code2_out, double *ws, hipStream_t st) {
-  // summation tree: level 1 over the scales, then over the partial sums
-  int64_t n = nblocks;
-  double *level = ws;
-  int64_t nout = (n + kFanIn - 1) / kFanIn;
-  hipLaunchKernelGGL(dq_sum_kernel<float>, dim3((unsigned)((nout + kSumRuns - 1) / kSumRuns)),
-                     dim3(256), 0, st, absmax, n, level, nblocks, offset);
+                               const Code2Table &code2, bool linear, uint8_t *q, float *absmax2,
+                               float *offset, float *code2_out, void *ws, hipStream_t st) {
+  double *levels = static_cast<double *>(ws);
+  const int64_t runs = (nblocks + kFanIn - 1) / kFanIn;
+  hipLaunchKernelGGL(dq_sum_kernel, dim3((unsigned)((runs + kSumRuns - 1) / kSumRuns)), dim3(256), 0,
+                     st, absmax, nblocks, levels, offset);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  while (nout > 1) {
-    double *next = level + nout;
-    const int64_t n2 = (nout + kFanIn - 1) / kFanIn;
-    hipLaunchKernelGGL(dq_sum_kernel<double>, dim3((unsigned)((n2 + kSumRuns - 1) / kSumRuns)),
-                       dim3(256), 0, st, level, nout, next, nblocks, offset);
+  if (runs > 1) {
+    hipLaunchKernelGGL(dq_top_kernel, dim3(1), dim3(256), 0, st, levels, runs, nblocks, offset);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    level = next;
-    nout = n2;
   }
   const int bs2 = 1 << log2bs2;
   const int E = bs2 > 2048 ? 16 : 8;
@@ -449,7 +507,7 @@ hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
 #define QMV_E(EV)                                                                          \
   hipLaunchKernelGGL(dq_encode_kernel<EV>, dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
-                     code2, offset, q, absmax2, code2_out)
+                     code2, linear ? 1 : 0, offset, q, absmax2, code2_out)
   if (E == 8) QMV_E(8); else QMV_E(16);
 #undef QMV_E
   return hipGetLastError();

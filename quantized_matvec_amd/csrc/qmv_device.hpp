@@ -61,6 +61,14 @@ __device__ __forceinline__ float block_scale(const Scales &s, int64_t b) {
 
 __device__ __forceinline__ float sc_offset(const Scales &s) { return s.offset[0]; }
 
+// A raw buffer resource over [base, base + bytes): loads past the end return
+// zero and move no data, so range checks need no branch (a branch around a
+// load makes the compiler wait for it right there).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }

@@ -290,10 +290,6 @@ template <int RPS>
 constexpr int m1_depth() { return RPS == 4 ? 1 : 2; }
 constexpr int kM1XLdsBytes = 90112;  // activations staged in LDS up to K = 45056 (whole slices)
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 template <int XDT, bool DQ, int XC, int RPS>  // XC: x chunks staged per thread (0: no staging)
 __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(

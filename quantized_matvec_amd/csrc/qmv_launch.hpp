@@ -29,9 +29,11 @@ hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int l
 
 size_t double_quant_workspace_bytes(int64_t nblocks);
 
+// ws: double_quant_workspace_bytes(nblocks) bytes for the partial sums.
+// linear: code2 is the default table (k - 127) / 127.
 hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,
-                               const Code2Table &code2, uint8_t *q, float *absmax2,
-                               float *offset, float *code2_out, double *ws, hipStream_t st);
+                               const Code2Table &code2, bool linear, uint8_t *q, float *absmax2,
+                               float *offset, float *code2_out, void *ws, hipStream_t st);
 
 hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t nblocks, float *out,
                                     hipStream_t st);
