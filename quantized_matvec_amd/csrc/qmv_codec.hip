@@ -536,14 +536,17 @@ hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t n, float 
 // ---------------------------------------------------------------------------
 // dequantize_4bit
 //
-// A thread handles 16-byte pieces (32 elements, always inside one block since
-// blocksize >= 32 and pieces are 32-aligned), U of them at a time with every
-// load issued before the first is used.  Each packed byte indexes a 256-entry
-// LDS table of fp32 code pairs; the two products with the block scale are
-// rounded once to fp32 and then converted (bf16: v_cvt_pk_bf16_f32, round to
-// nearest even, two elements per instruction).  Loads past the last full
-// piece are clamped to it (they are never stored), so the compiler can count
-// them; a ragged tail is written element by element by one thread.
+// A wave handles chunks of 2048 elements (1 KB packed).  Lane l reads the
+// 4-byte words at byte 256 w + 4 l of the chunk (w = 0..3), i.e. elements
+// 512 w + 8 l .. + 7, so that each of its output stores (8 elements) lands
+// next to its neighbours' and one store instruction writes a contiguous
+// range (16 B per lane for bf16 / fp16; lane-strided stores measured at half
+// the bandwidth).  U chunks per wave have all their loads issued before the
+// first is used; loads past the last full chunk are clamped to it (never
+// stored), so the compiler counts them.  Each packed byte indexes a 256-entry
+// LDS table of fp32 code pairs; the products with the block scale are rounded
+// once to fp32 and then converted (bf16: v_cvt_pk_bf16_f32, round to nearest
+// even).  Elements past the last full chunk are written by the tail loop.
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
@@ -560,7 +563,7 @@ __device__ __forceinline__ uint32_t cvt_pair(float lo, float hi) {
 }
 
 constexpr int kDeqThreads = 256;
-constexpr int kDeqU = 4;
+constexpr int kDeqU = 2;  // chunks in flight per wave
 
 template <int QT, int ODT, bool DQ>
 __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
@@ -570,6 +573,7 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
   __shared__ float2 lut2[256];  // byte -> (T[byte >> 4], T[byte & 15])
   __shared__ float code2[256];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   {
     const uint32_t *tb = table_bits(QT);
     lut2[tid] = make_float2(__uint_as_float(tb[tid >> 4]), __uint_as_float(tb[tid & 15]));
@@ -578,62 +582,75 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
   const float offset = DQ ? sc.offset[0] : 0.f;
   __syncthreads();
 
-  const int64_t nfull = numel >> 5;  // whole 16-byte pieces
-  const int64_t stride = (int64_t)gridDim.x * kDeqThreads;
-  for (int64_t base = (int64_t)blockIdx.x * kDeqThreads + tid; base < nfull; base += stride * kDeqU) {
-    uint4 p[kDeqU];
-    float sa[kDeqU];
-    uint32_t sq[kDeqU];
+  // 8 elements (one packed word) -> output
+  auto emit = [&](int64_t e, uint32_t word, float a) {
+    if constexpr (ODT == kF32) {
+      float o[8];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const float2 t = lut2[(word >> (8 * bb)) & 0xffu];
+        o[2 * bb] = t.x * a;
+        o[2 * bb + 1] = t.y * a;
+      }
+      float4 *dst = reinterpret_cast<float4 *>(out + e);
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    } else {
+      uint32_t o[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const float2 t = lut2[(word >> (8 * bb)) & 0xffu];
+        o[bb] = cvt_pair<ODT>(t.x * a, t.y * a);
+      }
+      *reinterpret_cast<uint4 *>(out + e) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  const int64_t nchunk = numel >> 11;
+  const int64_t wave = ((int64_t)blockIdx.x * kDeqThreads + tid) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kDeqThreads) >> 6;
+  const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
+  for (int64_t c0 = wave; c0 < nchunk; c0 += nwaves * kDeqU) {
+    uint32_t pw[kDeqU][4], sq[kDeqU][4];
+    float sa[kDeqU][4];
 #pragma unroll
     for (int u = 0; u < kDeqU; ++u) {
-      const int64_t c0 = base + u * stride;
-      const int64_t c = c0 < nfull ? c0 : nfull - 1;
-      p[u] = *reinterpret_cast<const uint4 *>(packed + (c << 4));
-      const int64_t b = (c << 5) >> log2bs;
-      if constexpr (DQ) {
-        sq[u] = sc.q[b];
-        sa[u] = sc.absmax2[b >> sc.log2bs2];
-      } else {
-        sa[u] = sc.absmax[b];
+      const int64_t cu = c0 + u * nwaves;
+      const int64_t c = cu < nchunk ? cu : nchunk - 1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pw[u][w] = pk[c * 256 + 64 * w + lane];
+        const int64_t b = ((c << 11) + 512 * w + 8 * lane) >> log2bs;
+        if constexpr (DQ) {
+          sq[u][w] = sc.q[b];
+          sa[u][w] = sc.absmax2[b >> sc.log2bs2];
+        } else {
+          sa[u][w] = sc.absmax[b];
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kDeqU; ++u) {
-      const int64_t c = base + u * stride;
-      if (c >= nfull) break;
-      const float a = DQ ? code2[sq[u]] * sa[u] + offset : sa[u];
-      const uint32_t pw[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
-      if constexpr (ODT == kF32) {
+      const int64_t c = c0 + u * nwaves;
+      if (c >= nchunk) break;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float o[8];
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const float2 t = lut2[(pw[w] >> (8 * bb)) & 0xffu];
-            o[2 * bb] = t.x * a;
-            o[2 * bb + 1] = t.y * a;
-          }
-          float4 *dst = reinterpret_cast<float4 *>(out + (c << 5) + 8 * w);
-          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t o[4];
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const float2 t = lut2[(pw[w] >> (8 * bb)) & 0xffu];
-            o[bb] = cvt_pair<ODT>(t.x * a, t.y * a);
-          }
-          *reinterpret_cast<uint4 *>(out + (c << 5) + 8 * w) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float a = DQ ? code2[sq[u][w]] * sa[u][w] + offset : sa[u][w];
+        emit((c << 11) + 512 * w + 8 * lane, pw[u][w], a);
       }
     }
   }
-  // ragged tail: elements [32 * nfull, numel), by one thread
-  if (blockIdx.x == 0 && tid == 0 && (numel & 31)) {
-    const int64_t e0 = nfull << 5;
+  // tail: elements [2048 nchunk, numel); whole 8-element words by any thread,
+  // the last (numel % 8) elements by one
+  const int64_t t0 = nchunk << 11;
+  const int64_t nword = (numel - t0) >> 3;
+  for (int64_t i = (int64_t)blockIdx.x * kDeqThreads + tid; i < nword;
+       i += (int64_t)gridDim.x * kDeqThreads) {
+    const int64_t e = t0 + 8 * i;
+    emit(e, pk[e >> 3], block_scale<DQ>(sc, e >> log2bs));
+  }
+  if (blockIdx.x == 0 && tid == 0 && (numel & 7)) {
+    const int64_t e0 = numel & ~int64_t(7);
     const float a = block_scale<DQ>(sc, e0 >> log2bs);
     for (int64_t e = e0; e < numel; ++e) {
       const uint32_t byte = packed[e >> 1];
@@ -660,8 +677,9 @@ static int device_cus() {
 template <int QT, int ODT>
 static hipError_t launch_dequant_t(const uint8_t *packed, const Scales &sc, bool dq, int64_t numel,
                                    int log2bs, void *out, hipStream_t st) {
-  const int64_t nfull = numel >> 5;
-  const int64_t want = (nfull + (int64_t)kDeqThreads * kDeqU - 1) / ((int64_t)kDeqThreads * kDeqU);
+  const int64_t nchunk = numel >> 11;
+  const int64_t waves_per_wg = kDeqThreads / 64;
+  const int64_t want = std::max<int64_t>(1, (nchunk + waves_per_wg * kDeqU - 1) / (waves_per_wg * kDeqU));
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 8 * device_cus()));
   if (dq)
     hipLaunchKernelGGL((dequantize_4bit_kernel<QT, ODT, true>), dim3(grid), dim3(kDeqThreads), 0, st,
