@@ -27,29 +27,59 @@ int log2_exact(int64_t v) {
 // Directed conversions used to turn an exact float64 threshold into an fp32
 // one that makes a single fp32 comparison exact.
 // ---------------------------------------------------------------------------
+// Written with selects only (no branches: they run once per threshold of
+// every block, in divergent lanes).
+//
+// Bits of the largest fp32 below f (f finite; below +-0 is -denorm_min).
 __device__ __forceinline__ uint32_t f32_step_down_bits(float f) {
   const uint32_t u = __float_as_uint(f);
-  if (f > 0.f) return u - 1u;
-  if (f == 0.f) return 0x80000001u;  // -denorm_min
-  return u + 1u;
+  const uint32_t away = (u >> 31) ? u + 1u : u - 1u;  // one step toward -inf
+  return (u & 0x7fffffffu) == 0u ? 0x80000001u : away;
 }
 
 // Largest fp32 <= d.
 __device__ __forceinline__ float f64_to_f32_rd(double d) {
   const float f = (float)d;  // round to nearest even
-  return ((double)f > d) ? __uint_as_float(f32_step_down_bits(f)) : f;
+  return (double)f > d ? __uint_as_float(f32_step_down_bits(f)) : f;
 }
 
 // Smallest fp32 >= d.
 __device__ __forceinline__ float f64_to_f32_ru(double d) {
   const float f = (float)d;
-  if ((double)f < d) {
-    const uint32_t u = __float_as_uint(f);
-    if (f > 0.f) return __uint_as_float(u + 1u);
-    if (f == 0.f) return __uint_as_float(0x00000001u);
-    return __uint_as_float(u - 1u);
-  }
-  return f;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t up = (u & 0x7fffffffu) == 0u ? 1u : ((u >> 31) ? u - 1u : u + 1u);
+  return (double)f < d ? __uint_as_float(up) : f;
+}
+
+// The fp32 threshold of the exact product p = absmax * mid: RD(p) when
+// mid > 0, pred(RU(p)) when mid < 0 (both roundings computed, one selected).
+__device__ __forceinline__ float threshold_f32(double p, bool pos) {
+  const float f = (float)p;  // round to nearest even
+  const double back = (double)f;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t down = f32_step_down_bits(f);
+  const uint32_t rd = back > p ? down : u;                          // RD(p)
+  const uint32_t up = (u & 0x7fffffffu) == 0u ? 1u : ((u >> 31) ? u - 1u : u + 1u);
+  const uint32_t ru = back < p ? up : u;                            // RU(p)
+  return __uint_as_float(pos ? rd : f32_step_down_bits(__uint_as_float(ru)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+// Max over aligned groups of G lanes (G a power of two, uniform): DPP moves
+// inside rows of 16, lane shuffles beyond.
+__device__ __forceinline__ float group_max(float m, int G) {
+  if (G >= 2) m = fmaxf(m, dpp_f32<0xb1>(m));   // quad_perm [1,0,3,2]
+  if (G >= 4) m = fmaxf(m, dpp_f32<0x4e>(m));   // quad_perm [2,3,0,1]
+  if (G >= 8) m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
+  if (G >= 16) m = fmaxf(m, dpp_f32<0x140>(m)); // row_mirror
+  if (G >= 32) m = fmaxf(m, __shfl_xor(m, 16));
+  if (G >= 64) m = fmaxf(m, __shfl_xor(m, 32));
+  return m;
 }
 
 // Rank among the thresholds (0..15 for NF4, 0..14 for FP4) -> code.
@@ -58,18 +88,21 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
   if constexpr (QT == kNF4) {
     return (uint32_t)r;  // NF4 codes are ascending ranks
   } else {
-    // FP4 ascending values: codes 15..9 (negatives), 0 (zero), 1..7 (positives)
-    return (uint32_t)(r < 7 ? 15 - r : (r == 7 ? 0 : r - 7));
+    // FP4 ascending values: codes 15..9 (negatives), 0 (zero), 1..7 (positives),
+    // as nibble r of one 64-bit constant
+    return (uint32_t)(0x76543210F9ABCDEFull >> (4 * r)) & 15u;
   }
 }
 
 // ---------------------------------------------------------------------------
 // quantize_4bit
 //
-// A workgroup of 256 threads takes a tile of 256 * E consecutive elements;
-// each thread owns E of them (one 16- or 32-byte load), so G = blocksize / E
-// neighbouring threads share a block.  The block absmax is reduced across
-// those G threads (wave shuffles, then LDS when a block spans waves).
+// A workgroup of 256 threads takes a tile of 256 * E consecutive elements
+// (E = 16: a 32-byte load for 16-bit inputs); G = blocksize / E neighbouring
+// threads share a block.  The block absmax is reduced across those G threads
+// (DPP moves within rows of 16 lanes, shuffles beyond, LDS when a block spans
+// waves).  The per-block threshold sets are double-buffered, so a tile needs
+// one barrier.
 //
 // Exact thresholds.  For each block the fp32 thresholds are derived from the
 // exact float64 products absmax * mid[j] (mid: midpoints of adjacent distinct
@@ -103,8 +136,10 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   constexpr int NT = QT == kNF4 ? 15 : 14;  // thresholds (FP4's +0 and -0 are one value)
   constexpr int TS = 17;                    // LDS floats per block: sentinels + thresholds
   const T *W = static_cast<const T *>(Wv);
-  __shared__ float wave_max[4];
-  __shared__ float thr[256 * E / 32 * TS];  // up to tile / 32 blocks per tile
+  // two sets, used by alternate tiles: a tile's thresholds are rewritten
+  // only after every thread has passed the next tile's barrier
+  __shared__ float wave_max[2][4];
+  __shared__ float thr[2][256 * E / 32 * TS];  // up to tile / 32 blocks per tile
   __shared__ uint32_t cand[32];
   __shared__ double mids[16];
   const int tid = threadIdx.x;
@@ -148,33 +183,31 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
 
   // FULL: a whole tile, whose stores are all unconditional (every lane of a
   // block writes the same absmax), so the load waits can be counted exactly
-  auto process = [&](int64_t t, const float (&v)[E], auto full_tag) {
+  auto process = [&](int64_t t, const float (&v)[E], int par, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t e0 = t * tile + (int64_t)tid * E;
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(v[i]));
-    const int gw = G < 64 ? G : 64;
-    for (int off = 1; off < gw; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    m = group_max(m, G);
     if (G > 64) {  // uniform across the launch
-      if (lane == 0) wave_max[wave] = m;
+      if (lane == 0) wave_max[par][wave] = m;
       __syncthreads();
       const int wpb = G >> 6;
       const int w0 = (wave / wpb) * wpb;
-      float mm = wave_max[w0];
-      for (int i = 1; i < wpb; ++i) mm = fmaxf(mm, wave_max[w0 + i]);
+      float mm = wave_max[par][w0];
+      for (int i = 1; i < wpb; ++i) mm = fmaxf(mm, wave_max[par][w0 + i]);
       m = mm;
     }
     if (FULL || (j_in_blk == 0 && e0 < numel)) absmax[e0 >> log2bs] = m;
 
     // this block's thresholds, shared out among its G threads
-    float *bt = thr + blk_in_tile * TS;
+    float *bt = thr[par] + blk_in_tile * TS;
     const double ad = (double)m;
     for (int j = j_in_blk; j < NT; j += G) {
       const double mid = mids[j];
       const double p = ad * mid;  // exact
-      bt[1 + j] = mid > 0.0 ? f64_to_f32_rd(p)
-                            : __uint_as_float(f32_step_down_bits(f64_to_f32_ru(p)));
+      bt[1 + j] = threshold_f32(p, mid > 0.0);
     }
     if (j_in_blk == 0) {
       bt[0] = -INFINITY;
@@ -186,12 +219,11 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
     // so the reciprocal stays finite, huge ones down by 2^100 so it stays
     // normal (only the candidate uses n); an all-zero block has n = 0
     const float sc = m < 0x1p-100f ? 0x1p100f : (m > 0x1p100f ? 0x1p-100f : 1.f);
-    const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m * sc) : 0.f;
+    const float inv16 = m > 0.f ? 16.f * __builtin_amdgcn_rcpf(m * sc) : 0.f;
     uint32_t code[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const float n = (v[i] * sc) * inv;
-      int bin = (int)fmaf(n, 16.f, 16.f);
+      int bin = (int)fmaf(v[i] * sc, inv16, 16.f);  // 16 (n + 1), n ~ x / absmax
       bin = bin < 0 ? 0 : (bin > 31 ? 31 : bin);
       const int c = (int)cand[bin];
       const float lo = bt[c], hi = bt[c + 1];  // t_(c-1), t_c
@@ -220,13 +252,13 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       for (int b = 0; b < E / 2; ++b)
         if (e0 + 2 * b < numel) dst[b] = (uint8_t)(word[b >> 2] >> (8 * (b & 3)));
     }
-    __syncthreads();  // thr and wave_max are reused by the next tile
   };
 
   // full tiles: the next tile's loads are issued before this one is processed
   // (unconditionally, clamped to the last full tile, so the waits are exact)
   const int64_t nfull = numel / tile;
   int64_t t = blockIdx.x;
+  int par = 0;
   if (nfull > 0) {
     uint4 nx[NW];
     load_full(t < nfull ? t : nfull - 1, nx);
@@ -235,7 +267,8 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       convert(nx, v);
       const int64_t tn = t + gridDim.x;
       load_full(tn < nfull ? tn : nfull - 1, nx);
-      process(t, v, std::true_type{});
+      process(t, v, par, std::true_type{});
+      par ^= 1;
     }
   }
   // the ragged last tile, if any (same workgroup stride, so exactly one takes it)
@@ -244,23 +277,20 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
     float v[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (e0 + i < numel) ? load_elem<DT>(W, e0 + i) : 0.f;
-    process(t, v, std::false_type{});
+    process(t, v, par, std::false_type{});
   }
 }
 
 template <int DT, int QT>
 static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, const QuantArgs &qa,
                                     uint8_t *packed, float *absmax, hipStream_t st) {
-  const int E = log2bs > 11 ? 16 : 8;  // a tile always holds whole blocks
+  // 16 elements per thread: a tile (4096) holds whole blocks of every size
+  constexpr int E = 16;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, 8 * device_cus()));
-  if (E == 8)
-    hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, 8>), dim3(grid), dim3(256), 0, st, W, numel,
-                       log2bs, qa, packed, absmax);
-  else
-    hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, 16>), dim3(grid), dim3(256), 0, st, W, numel,
-                       log2bs, qa, packed, absmax);
+  hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, E>), dim3(grid), dim3(256), 0, st, W, numel,
+                     log2bs, qa, packed, absmax);
   return hipGetLastError();
 }
 
