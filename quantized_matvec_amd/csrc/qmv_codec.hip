@@ -90,7 +90,7 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
   } else {
     // FP4 ascending values: codes 15..9 (negatives), 0 (zero), 1..7 (positives),
     // as nibble r of one 64-bit constant
-    return (uint32_t)(0x76543210F9ABCDEFull >> (4 * r)) & 15u;
+    return (uint32_t)(0x0765432109ABCDEFull >> (4 * r)) & 15u;
   }
 }
 
