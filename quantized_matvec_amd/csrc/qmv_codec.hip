@@ -65,21 +65,23 @@ __device__ __forceinline__ float threshold_f32(double p, bool pos) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xf, 0xf, false));
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
 }
 
-// Max over aligned groups of G lanes (G a power of two, uniform): DPP moves
-// inside rows of 16, lane shuffles beyond.
+// Max over aligned groups of G lanes (G a power of two, uniform) of a
+// non-negative float, compared as unsigned bits (same order, and no NaN
+// canonicalisation around each step): DPP moves inside rows of 16 lanes,
+// lane shuffles beyond.
 __device__ __forceinline__ float group_max(float m, int G) {
-  if (G >= 2) m = fmaxf(m, dpp_f32<0xb1>(m));   // quad_perm [1,0,3,2]
-  if (G >= 4) m = fmaxf(m, dpp_f32<0x4e>(m));   // quad_perm [2,3,0,1]
-  if (G >= 8) m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
-  if (G >= 16) m = fmaxf(m, dpp_f32<0x140>(m)); // row_mirror
-  if (G >= 32) m = fmaxf(m, __shfl_xor(m, 16));
-  if (G >= 64) m = fmaxf(m, __shfl_xor(m, 32));
-  return m;
+  uint32_t u = __float_as_uint(m);
+  if (G >= 2) u = max(u, dpp_u32<0xb1>(u));   // quad_perm [1,0,3,2]
+  if (G >= 4) u = max(u, dpp_u32<0x4e>(u));   // quad_perm [2,3,0,1]
+  if (G >= 8) u = max(u, dpp_u32<0x141>(u));  // row_half_mirror
+  if (G >= 16) u = max(u, dpp_u32<0x140>(u)); // row_mirror
+  if (G >= 32) u = max(u, (uint32_t)__shfl_xor((int)u, 16));
+  if (G >= 64) u = max(u, (uint32_t)__shfl_xor((int)u, 32));
+  return __uint_as_float(u);
 }
 
 // Rank among the thresholds (0..15 for NF4, 0..14 for FP4) -> code.
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   // only after every thread has passed the next tile's barrier
   __shared__ float wave_max[2][4];
   __shared__ float thr[2][256 * E / 32 * TS];  // up to tile / 32 blocks per tile
-  __shared__ uint32_t cand[32];
+  __shared__ uint8_t cand[32];  // bytes: the bin is the address
   __shared__ double mids[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
