@@ -7,6 +7,9 @@
 // bit-exact: the nearest-code decision is made against exact thresholds, and
 // every float operation is an explicitly rounded one.
 #include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "qmv_launch.hpp"
@@ -117,15 +120,23 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
 // table's code.  The G threads of a block compute its thresholds together
 // and leave them in LDS as [-inf, t_0, ..., t_last, +inf].
 //
-// Rank.  n = x / absmax is approximated in fp32 and rounded into one of 32
-// bins of width 1/16 on [-1, 1]; a small table gives the rank at the bin's
-// centre.  Adjacent thresholds are more than 1/16 apart (in n), so the true
-// rank differs from that candidate c by at most one, and two exact
-// comparisons settle it: rank = c + [x > t_c] - [x <= t_(c-1)].
+// Rank.  n = x / absmax is approximated in fp32 and placed in a bin of
+// width 1 / S: bin = floor(S n + O).  The host picks S and O so that every
+// bin holds at most one midpoint and every midpoint lies well inside its bin
+// (at least a few hundredths of a bin from either edge, against an error in
+// S n + O of a few millionths).  With J(b) = the number of thresholds below
+// the lower edge of bin b, the rank of x is J(b) + [x > t_J(b)]: when the bin
+// holds threshold J(b) the compare decides it exactly; when it holds none,
+// t_J(b) lies above the bin and the compare is false.  An element whose
+// approximate n falls in the neighbouring bin is within a few millionths of
+// an edge, where no threshold is, so the count is the same.  t_NT = +inf.
 // ---------------------------------------------------------------------------
+constexpr int kQBins = 64;
 struct QuantArgs {
   Midpoints4 mids;
-  uint8_t cand[32];  // rank at the centre of bin b: n = -1 + (b + 0.5) / 16
+  uint8_t cand[kQBins];  // J(b)
+  float bin_scale;       // S
+  float bin_offset;      // O
 };
 
 template <int DT, int QT, int E>
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   // only after every thread has passed the next tile's barrier
   __shared__ float wave_max[2][4];
   __shared__ float thr[2][256 * E / 32 * TS];  // up to tile / 32 blocks per tile
-  __shared__ uint8_t cand[32];  // bytes: the bin is the address
+  __shared__ uint8_t cand[kQBins];  // bytes: the bin is the address
   __shared__ double mids[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   const int blk_in_tile = tid / G;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
-  if (tid < 32) cand[tid] = qa.cand[tid];
+  if (tid < kQBins) cand[tid] = qa.cand[tid];
   if (tid < NT) mids[tid] = qa.mids.mid[tid];
   __syncthreads();
 
@@ -221,15 +232,14 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
     // so the reciprocal stays finite, huge ones down by 2^100 so it stays
     // normal (only the candidate uses n); an all-zero block has n = 0
     const float sc = m < 0x1p-100f ? 0x1p100f : (m > 0x1p100f ? 0x1p-100f : 1.f);
-    const float inv16 = m > 0.f ? 16.f * __builtin_amdgcn_rcpf(m * sc) : 0.f;
+    const float inv = m > 0.f ? qa.bin_scale * __builtin_amdgcn_rcpf(m * sc) : 0.f;
     uint32_t code[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      int bin = (int)fmaf(v[i] * sc, inv16, 16.f);  // 16 (n + 1), n ~ x / absmax
-      bin = bin < 0 ? 0 : (bin > 31 ? 31 : bin);
+      int bin = (int)fmaf(v[i] * sc, inv, qa.bin_offset);  // S n + O
+      bin = bin < 0 ? 0 : (bin > kQBins - 1 ? kQBins - 1 : bin);
       const int c = (int)cand[bin];
-      const float lo = bt[c], hi = bt[c + 1];  // t_(c-1), t_c
-      const int r = c + (v[i] > hi ? 1 : 0) - (v[i] <= lo ? 1 : 0);
+      const int r = c + (v[i] > bt[1 + c] ? 1 : 0);
       code[i] = (FULL || e0 + i < numel) ? rank_to_code<QT>(r) : 0u;
     }
 
@@ -296,18 +306,66 @@ static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, co
   return hipGetLastError();
 }
 
+// Bin geometry of the rank search (see above): S in 14..30 bins per unit of
+// n and offset O = S + 1 + k / 64 + 1 / 128, chosen so that no two midpoints
+// share a bin and the midpoint nearest to a bin edge is as far from it as
+// possible (at least 0.02 bin); J(b) counts the midpoints below bin b.
+// Bins of n in [-1, 1] are 1 .. 2 S + 2 < kQBins.
+static bool bin_geometry(const Midpoints4 &m, int nt, QuantArgs &qa) {
+  double best = 0.0;
+  for (int S = 14; S <= 30; ++S) {
+    for (int k = 0; k < 64; ++k) {
+      const double o = S + 1 + k / 64.0 + 1.0 / 128.0;
+      double worst = 1.0;
+      long prev = -1;
+      bool distinct = true;
+      for (int j = 0; j < nt; ++j) {
+        const double v = S * m.mid[j] + o;
+        const double b = std::floor(v);
+        worst = std::min(worst, std::min(v - b, b + 1.0 - v));
+        distinct = distinct && (long)b != prev;
+        prev = (long)b;
+      }
+      if (distinct && worst > best) {
+        best = worst;
+        qa.bin_scale = (float)S;
+        qa.bin_offset = (float)o;
+      }
+    }
+  }
+  if (best < 0.02) return false;
+  for (int b = 0; b < kQBins; ++b) {
+    int c = 0;
+    for (int j = 0; j < nt; ++j)
+      c += std::floor((double)qa.bin_scale * m.mid[j] + (double)qa.bin_offset) < b ? 1 : 0;
+    qa.cand[b] = (uint8_t)c;
+  }
+  return true;
+}
+
 hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int log2bs, int qt,
                                 const Midpoints4 &m, uint8_t *packed, float *absmax,
                                 hipStream_t st) {
   // candidate rank at each bin centre, from the exact midpoints
-  QuantArgs qa{};
-  qa.mids = m;
+  // the geometry depends only on the table: found once per table
+  static std::mutex mu;
+  static Midpoints4 cached_m[2];
+  static QuantArgs cached_qa[2];
+  static bool cached_ok[2] = {false, false};
   const int nt = qt == kNF4 ? 15 : 14;
-  for (int b = 0; b < 32; ++b) {
-    const double centre = -1.0 + (b + 0.5) / 16.0;
-    int c = 0;
-    for (int j = 0; j < nt; ++j) c += m.mid[j] < centre ? 1 : 0;
-    qa.cand[b] = (uint8_t)c;
+  QuantArgs qa{};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const int i = qt == kNF4 ? 0 : 1;
+    if (!cached_ok[i] || memcmp(&cached_m[i], &m, sizeof(m)) != 0) {
+      QuantArgs g{};
+      g.mids = m;
+      if (!bin_geometry(m, nt, g)) return hipErrorInvalidValue;
+      cached_m[i] = m;
+      cached_qa[i] = g;
+      cached_ok[i] = true;
+    }
+    qa = cached_qa[i];
   }
 #define QMV_Q(DT, QT) return launch_quantize_t<DT, QT>(W, numel, log2bs, qa, packed, absmax, st)
   if (qt == kNF4) {
