@@ -188,14 +188,180 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny M (M <= 32 MT): gemm_4bit_skinny_kernel
+//
+// A workgroup of KW waves owns 32 output columns (weight rows n0 .. n0 + 31)
+// and all M rows (MT tiles of 32); its waves split K (wave w takes the 64-wide
+// k-steps w, w + KW, ...) and their partial tiles are summed through LDS at
+// the end, in wave order.  With N / 32 workgroups the grid fills the GPU even
+// for a handful of rows.
+//
+// No LDS staging: each lane loads exactly its operands of
+// v_mfma_f32_32x32x16_bf16.  In k-step s lane l covers column n0 + l % 32 and
+// the 32 k-values 64 s + 32 (l / 32) .. + 31 (one 16-byte packed load, one
+// block scale); the order of k inside the four MFMAs of the step is chosen so
+// that MFMA j takes that lane's k-values 8 j .. 8 j + 7 (a sum does not depend
+// on the order of its terms, and A is read in the same order), so every
+// operand is a contiguous 16 bytes.  The weights are dequantized in registers
+// exactly as in the tile kernel (fp32(T * a_hat) rounded to bf16).  The next
+// step's loads are issued before the current step is computed.
+// ---------------------------------------------------------------------------
+template <int CDT, bool DQ, int MT, int KW>
+__global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
+    const uint16_t *__restrict__ A, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    Scales sc, int log2bs, Table16f table, void *__restrict__ Cv) {
+  using CT = typename Storage<CDT>::type;
+  CT *C = static_cast<CT *>(Cv);
+  __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
+  __shared__ float code2[256];
+  __shared__ float red[(KW - 1) * MT * 16 * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < 256; i += 64 * KW) {
+    lut2[i] = make_float2(table.v[i >> 4], table.v[i & 15]);
+    if constexpr (DQ) code2[i] = sc.code2[i];
+  }
+  const float offset = DQ ? sc.offset[0] : 0.f;
+  __syncthreads();
+
+  const int kh = lane >> 5;
+  const int col = lane & 31;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t n = n0 + col;
+  const int64_t nc = n < N ? n : N - 1;  // columns past N are computed, never stored
+  const int64_t nsteps = (K + 63) >> 6;
+  // Workgroup-uniform bounded buffers (the host keeps every offset below 2^31
+  // and K a multiple of 64): rows of A past M and weight rows past N read as
+  // zeros.  The prefetch past a wave's last step reads whatever lies there (or
+  // zeros) and is never used.
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const __amdgpu_buffer_rsrc_t prs =
+      make_rsrc(packed + n0 * (int64_t)rowb, (uint32_t)((N - n0 < 32 ? N - n0 : 32) * rowb));
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A, (uint32_t)(M * K * 2));
+  const uint32_t poff = (uint32_t)col * rowb + 16u * kh;
+  const uint32_t aoff = (uint32_t)(col * K * 2) + 64u * kh;
+  const uint32_t atile = (uint32_t)(32 * K * 2);
+
+  struct Regs {
+    uint4 p;
+    uint4 a[MT][4];
+    uint32_t q;
+    float s;
+  };
+  auto load = [&](int64_t st, Regs &r) {
+    r.p = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, poff + (uint32_t)(32 * st), 0, 0));
+    const uint32_t ao = aoff + (uint32_t)(128 * st);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        r.a[t][j] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, ao + t * atile, 16 * j, 0));
+    const int64_t sl = st < nsteps ? st : nsteps - 1;
+    const int64_t b = (nc * K + 64 * sl + 32 * kh) >> log2bs;
+    if constexpr (DQ) {
+      r.q = sc.q[b];
+      r.s = sc.absmax2[b >> sc.log2bs2];
+    } else {
+      r.s = sc.absmax[b];
+    }
+  };
+
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+
+  auto compute = [&](const Regs &r) {
+    const float a = DQ ? code2[r.q] * r.s + offset : r.s;
+    const uint32_t pw[4] = {r.p.x, r.p.y, r.p.z, r.p.w};
+    float2 tv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tv[4 * j + q] = lut2[(pw[j] >> (8 * q)) & 0xffu];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t bw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // dequantized weights: fp32(T * a_hat) rounded to bf16 (nearest even)
+        const f32x2_t v = {materialize(tv[4 * j + q].x * a), materialize(tv[4 * j + q].y * a)};
+        bw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+      }
+      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, r.a[t][j]), bop,
+                                                         acc[t], 0, 0, 0);
+    }
+  };
+
+  // two register sets: step s + KW is loaded while step s is computed.  No
+  // branch separates a load from the computation it feeds (a load that could
+  // be moved past the computation before it would be issued late).
+  const int64_t nw = nsteps > wave ? (nsteps - wave + KW - 1) / KW : 0;  // this wave's steps
+  Regs r0, r1;
+  load(wave, r0);
+  int64_t i = 0;
+  for (; i + 1 < nw; i += 2) {
+    load(wave + (i + 1) * KW, r1);
+    compute(r0);
+    load(wave + (i + 2) * KW, r0);
+    compute(r1);
+  }
+  if (i < nw) compute(r0);
+
+  // sum the waves' partial tiles (wave order) and store
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[(((wave - 1) * MT + t) * 16 + i) * 64 + lane] = acc[t][i];
+  }
+  __syncthreads();
+  if (wave == 0 && n < N) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = acc[t][i];
+        for (int w = 1; w < KW; ++w) v += red[(((w - 1) * MT + t) * 16 + i) * 64 + lane];
+        // accumulator layout: column = lane % 32, row = 8 (i / 4) + 4 (lane / 32) + i % 4
+        const int64_t m = 32 * t + 8 * (i >> 2) + 4 * kh + (i & 3);
+        if (m < M) store_elem<CDT>(C, m * N + n, v);
+      }
+  }
+}
+
 hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
                             const Scales &sc, bool dq, int log2bs, int qt, void *C, int c_dtype,
                             hipStream_t st) {
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   const uint16_t *a = static_cast<const uint16_t *>(A);
   Table16f table;
   const uint32_t *bits = table_bits(qt);
   for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
+  if (M <= 64 && K % 64 == 0 && K < (1 << 23)) {  // skinny M: N / 32 workgroups of 8 waves splitting K
+    const dim3 sgrid((unsigned)((N + 31) / 32));
+#define QMV_S(CDT, DQV, MTV)                                                                   \
+  hipLaunchKernelGGL((gemm_4bit_skinny_kernel<CDT, DQV, MTV, 8>), sgrid, dim3(512), 0, st, a, M, \
+                     N, K, packed, sc, log2bs, table, C)
+#define QMV_SM(CDT, DQV) \
+  if (M <= 32) { QMV_S(CDT, DQV, 1); } else { QMV_S(CDT, DQV, 2); }
+#define QMV_SD(CDT) \
+  if (dq) { QMV_SM(CDT, true); } else { QMV_SM(CDT, false); }
+    if (c_dtype == kF32) { QMV_SD(kF32); }
+    else if (c_dtype == kF16) { QMV_SD(kF16); }
+    else { QMV_SD(kBF16); }
+#undef QMV_SD
+#undef QMV_SM
+#undef QMV_S
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
 #define QMV_M(CDT, DQV)                                                                        \
   hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV>), grid, dim3(256), 0, st, a, M, N, K, packed, \
                      sc, log2bs, table, C)

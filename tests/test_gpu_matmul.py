@@ -173,17 +173,41 @@ def test_gemm_full_output(M, qt, dq):
     assert rel_l2(f64(Cf), ref) <= 1e-2
 
 
+@pytest.mark.parametrize("rows", [20, 64, 200])
 @pytest.mark.parametrize("qt", ["nf4", "fp4"])
-def test_gemm_identity_rows_exact(qt):
+def test_gemm_identity_rows_exact(qt, rows):
+    """Rows of the identity pick rows of the bf16 dequantized weight; every
+    other product is an exact zero, so any order of summation is exact (the
+    short cases run the split-K kernel, 200 rows the tile kernel)."""
     N, K = 300, 256
     W = gaussian((N, K), 0.02, 9, "bf16")
     p_ref, a_ref = O.quantize_4bit(f64(W), 64, qt)
     packed, st = upload_state(p_ref, a_ref, (N, K), torch.bfloat16, 64, qt)
-    A = torch.eye(K, dtype=torch.bfloat16)[:200]
+    A = torch.eye(K, dtype=torch.bfloat16)[:rows]
     C = qmv.gemm_4bit(A.cuda(), packed, st).cpu()
     What = O.dequantize_4bit(p_ref, a_ref, N * K, 64, qt, "bf16").reshape(N, K)
     got = C.view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(got, What[:, :200].T)
+    assert np.array_equal(got, What[:, :rows].T)
+
+
+@pytest.mark.parametrize("M", [2, 31, 32, 33, 64, 65])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemm_skinny_ragged(M, dq):
+    """Row counts around the 32-row tiles of the split-K kernel (and 65, the
+    first of the tile kernel); K = 96 with block 32 ends on half a 64-wide
+    k-step and N = 70 on a partial group of 32 output features."""
+    N, K, bs = 70, 96, 32
+    W = gaussian((N, K), 0.02, 40 + M, "bf16")
+    A = gaussian((M, K), 1.0, 41 + M, "bf16")
+    p_ref, ahat = oracle_state(f64(W), bs, "nf4", dq, bs2=32)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "nf4", double_quant=dq, blocksize2=32)
+    ref = O.matmul_4bit(f64(A), p_ref, ahat, N, K, bs, "nf4")
+    # the products are bf16 MFMAs of bf16-rounded weights: the bf16 bound
+    # applies to the fp32 output as well (as in test_gemm_full_output)
+    for od, tol in ((torch.float32, 1e-2), (torch.bfloat16, 2e-2)):
+        C = qmv.gemm_4bit(A.cuda(), packed, st, out_dtype=od)
+        assert C.shape == (M, N)
+        assert rel_l2(f64(C), ref) <= tol, (M, dq, od)
 
 
 def test_gemm_m1_matches_gemv():
