@@ -173,12 +173,13 @@ def test_gemm_full_output(M, qt, dq):
     assert rel_l2(f64(Cf), ref) <= 1e-2
 
 
-@pytest.mark.parametrize("rows", [20, 64, 200])
+@pytest.mark.parametrize("rows", [64, 200])
 @pytest.mark.parametrize("qt", ["nf4", "fp4"])
 def test_gemm_identity_rows_exact(qt, rows):
     """Rows of the identity pick rows of the bf16 dequantized weight; every
-    other product is an exact zero, so any order of summation is exact (the
-    short cases run the split-K kernel, 200 rows the tile kernel)."""
+    other product is an exact zero, so any order of summation is exact (64
+    rows run the split-K kernel, 200 rows the tile kernel: both multiply
+    bf16-rounded dequantized weights)."""
     N, K = 300, 256
     W = gaussian((N, K), 0.02, 9, "bf16")
     p_ref, a_ref = O.quantize_4bit(f64(W), 64, qt)
@@ -190,13 +191,40 @@ def test_gemm_identity_rows_exact(qt, rows):
     assert np.array_equal(got, What[:, :rows].T)
 
 
-@pytest.mark.parametrize("M", [2, 31, 32, 33, 64, 65])
+@pytest.mark.parametrize("rows", [1, 8, 16, 20, 32])
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_gemm_narrow_identity_rows_exact(qt, rows):
+    """Up to 32 rows and blocks of 64 or more take the narrow kernel, which
+    multiplies bf16-rounded code values by the activations and applies the
+    block scale per 64 k-values in fp32: a row of the identity then returns
+    fp32(a_hat * bf16(T[code])) bit for bit (a zero of either sign reads +0,
+    the sum of the other exact zeros), and its bf16 rounding."""
+    N, K, bs = 300, 256, 64
+    W = gaussian((N, K), 0.02, 19, "bf16")
+    p_ref, a_ref = O.quantize_4bit(f64(W), bs, qt)
+    packed, st = upload_state(p_ref, a_ref, (N, K), torch.bfloat16, bs, qt)
+    A = torch.eye(K, dtype=torch.bfloat16)[3:3 + rows]
+    t16 = O.f32_to_bf16_bits(O.code_table(qt).astype(np.float32)).astype(np.uint32) << np.uint32(16)
+    codes = O.unpack_nibbles(p_ref, N * K).reshape(N, K)
+    scale = np.repeat(a_ref.astype(np.float32).reshape(N, K // bs), bs, axis=1)
+    w = t16.view(np.float32)[codes] * scale + np.float32(0)  # fp32 products, -0 -> +0
+    want = np.ascontiguousarray(w[:, 3:3 + rows].T)
+    C = qmv.gemm_4bit(A.cuda(), packed, st, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(C.view(np.uint32), want.view(np.uint32))
+    Cb = qmv.gemm_4bit(A.cuda(), packed, st).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(Cb, O.f32_to_bf16_bits(want))
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 9, 16, 17, 31, 32, 33, 64, 65])
+@pytest.mark.parametrize("K", [96, 192, 1600])
 @pytest.mark.parametrize("dq", [False, True])
-def test_gemm_skinny_ragged(M, dq):
-    """Row counts around the 32-row tiles of the split-K kernel (and 65, the
-    first of the tile kernel); K = 96 with block 32 ends on half a 64-wide
-    k-step and N = 70 on a partial group of 32 output features."""
-    N, K, bs = 70, 96, 32
+def test_gemm_skinny_ragged(M, K, dq):
+    """Row counts around the row tiles of the split-K kernels (8, 16, 32 and
+    64 rows; 65 is the first of the tile kernel).  N = 70 ends on a partial
+    group of 32 output features.  K = 96 (block 32) is not a whole number of
+    64-wide k-steps and takes the tile kernel; K = 192 leaves a wave with no
+    k-step, K = 1600 gives the waves 7 or 6 steps each."""
+    N, bs = 70, 32
     W = gaussian((N, K), 0.02, 40 + M, "bf16")
     A = gaussian((M, K), 1.0, 41 + M, "bf16")
     p_ref, ahat = oracle_state(f64(W), bs, "nf4", dq, bs2=32)
