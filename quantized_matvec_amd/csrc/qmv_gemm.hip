@@ -339,35 +339,37 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Narrow M (M <= MP <= 32, blocks of 64 or more): gemm_4bit_narrow_kernel
+// Narrow M (M <= MP <= 16, blocks of 64 or more): gemm_4bit_narrow_kernel
 //
 // A workgroup of KW waves owns 32 output columns (weight rows n0 .. n0 + 31);
-// wave w takes the 64-wide k-steps w, w + KW, ... and the waves' partial
-// tiles are summed through LDS at the end, in wave order.  With N / 32
-// workgroups the grid fills the GPU even for a handful of rows.
+// wave w takes a contiguous share of K, in groups of two 64-wide k-steps, and
+// the waves' partial tiles are summed through LDS at the end, in wave order.
+// With N / 32 workgroups the grid fills the GPU even for a handful of rows.
 //
-// Fewest instructions per weight:
+//  * A group's weights (32 rows x 64 bytes) and activations (MP rows x 128
+//    k-values) go to a private LDS slot of the wave through LDS-direct buffer
+//    loads: the weight loads read 64 contiguous bytes of each of 16 rows per
+//    instruction, and nothing in flight holds registers.  NB slots form a
+//    ring, NB - 1 groups are in flight, and as loads complete in issue order
+//    a wave waits for exactly the oldest group it has in flight.
 //  * One v_mfma_f32_32x32x16_bf16 takes, per lane, 8 k-values of one column;
-//    the lane's 16-byte weight load holds the 32 k-values of its half of a
-//    step (MFMA j takes values 8 j .. 8 j + 7 of it, and the activations are
-//    read in the same order, so the sum is unchanged).  A packed byte is
-//    decoded by one LDS lookup into the bf16 pair of its two code values.
+//    lane (column c, half h) holds the 32 k-values 32 h .. 32 h + 31 of a
+//    step, and MFMA j takes values 8 j .. 8 j + 7 of them, with the
+//    activations read in the same order (the sum is unchanged).  A packed
+//    byte is decoded by one LDS lookup into the bf16 pair of its two code
+//    values.
 //  * A 64-wide step lies inside one block (block size >= 64), so the four
 //    MFMAs of a step sum code value x activation into a fresh tile, and the
 //    block scale is applied once per step and column, in fp32, as that tile
 //    is added to the accumulator.  Only accumulator registers that can hold a
 //    row below MP are scaled, reduced and stored.
-//  * NB - 1 steps per wave are in flight: weight codes and scales go to a
-//    ring of NB register sets, the step's activations (MP rows x 64 k) to a
-//    ring of NB private LDS slots through LDS-direct buffer loads, so they
-//    hold no registers while in flight.  Loads complete in issue order, so a
-//    wave waits for exactly the oldest step it has in flight.
 //
-// Activation layout in a slot: chunk c (16 bytes, 8 k-values) holds row
-// m = c % MP, half kh and MFMA j given by c / MP = 2 j + kh, i.e. exactly
-// the 16 bytes lane (kh, m) feeds MFMA j; one more chunk at the end is zero
-// and feeds the lanes of rows MP .. 31.  One LDS-direct load moves 64
-// consecutive chunks.
+// Slot layout, in 16-byte chunks: 128 weight chunks, chunk 4 r + (p ^ f(r))
+// holding 16-byte piece p of row r, f(r) = (r / 4) % 4 (the xor spreads the
+// reads of one MFMA operand over the LDS banks); then 16 MP activation
+// chunks, chunk ((t * 4 + j) * 2 + h) * MP + m holding the 8 k-values of row
+// m that lane (m, h) feeds MFMA j of step t; then one zero chunk, read by
+// the lanes of rows MP .. 31.
 // ---------------------------------------------------------------------------
 template <int N_, class F, int... Us>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Us...>) {
@@ -389,12 +391,13 @@ template <int CDT, bool DQ, int MP, int NB, int KW>
 __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
     const uint16_t *__restrict__ A, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     Scales sc, int log2bs, Table16f table, void *__restrict__ Cv) {
-  constexpr int CH = 8 * MP;            // 16-byte activation chunks per step
-  constexpr int ND = CH / 64;           // LDS-direct loads per step
-  constexpr int SLOT = CH + 1;          // + the zero chunk
+  constexpr int WCH = 128;              // weight chunks per group (32 rows x 64 bytes)
+  constexpr int ACH = 16 * MP;          // activation chunks per group (MP rows x 128 k-values)
+  constexpr int WND = WCH / 64, AND = ACH / 64;  // LDS-direct loads per group
+  constexpr int SLOT = WCH + ACH + 1;   // + the zero chunk
   constexpr int RR = MP / 2;            // accumulator registers holding rows < MP
-  constexpr int PER = ND + 1 + (DQ ? 2 : 1);  // loads per step
-  static_assert(MP % 8 == 0 && MP <= 32 && NB >= 2 && NB <= 8 && (NB - 1) * PER < 64 && KW >= 4,
+  constexpr int PER = WND + AND + (DQ ? 4 : 2);  // loads per group
+  static_assert(MP % 4 == 0 && MP <= 16 && NB >= 2 && NB <= 8 && (NB - 1) * PER < 64 && KW >= 4,
                 "narrow gemm shape");
   using CT = typename Storage<CDT>::type;
   CT *C = static_cast<CT *>(Cv);
@@ -423,25 +426,38 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
   const int64_t n = n0 + col;
   const int64_t nc = n < N ? n : N - 1;  // columns past N are computed, never stored
   const int64_t nsteps = K >> 6;         // K % 64 == 0 (host)
-  const int64_t nw = nsteps > wave ? (nsteps - wave + KW - 1) / KW : 0;  // this wave's steps
+  const int64_t ngroups = (nsteps + 1) >> 1;
+  const int64_t qg = ngroups / KW, rg = ngroups % KW;
+  const int64_t g0 = wave * qg + (wave < rg ? wave : rg);  // this wave's groups: g0 .. g0 + nw - 1
+  const int64_t nw = qg + (wave < rg ? 1 : 0);
   // Bounded buffers, uniform per workgroup (the host keeps offsets below
   // 2^31): activation rows past M and weight rows past N read as zeros.
-  // Loads for steps past the wave's last one read whatever lies in range
-  // (or zeros) and are never used.
+  // Loads past the wave's last group (or past the end of a row) read
+  // whatever lies in range, or zeros, and are never used.
   const uint32_t rowb = (uint32_t)(K >> 1);
   const __amdgpu_buffer_rsrc_t prs =
       make_rsrc(packed + n0 * (int64_t)rowb, (uint32_t)((N - n0 < 32 ? N - n0 : 32) * rowb));
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(A, (uint32_t)(M * K * 2));
-  const uint32_t poff = (uint32_t)col * rowb + 16u * kh;
-  uint32_t goff[ND];  // activation chunk this lane moves in LDS-direct load d (step 0)
+  uint32_t woff[WND];  // weight piece this lane moves in LDS-direct load d (group 0)
 #pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const int c = 64 * d + lane, m = c % MP, q = c / MP;
-    goff[d] = (uint32_t)(m * K * 2) + 64u * (q & 1) + 16u * (q >> 1);
+  for (int d = 0; d < WND; ++d) {
+    const int r = 16 * d + (lane >> 2);
+    woff[d] = (uint32_t)r * rowb + 16u * ((lane & 3) ^ ((r >> 2) & 3));
   }
-  int rd[4];  // chunk this lane reads for MFMA j
+  uint32_t aoff[AND];  // activation chunk this lane moves in LDS-direct load d (group 0)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) rd[j] = col < MP ? (j * 2 + kh) * MP + col : CH;
+  for (int d = 0; d < AND; ++d) {
+    const int c = 64 * d + lane, m = c % MP, q = c / MP;
+    aoff[d] = (uint32_t)(m * K * 2) + 128u * (q >> 3) + 64u * (q & 1) + 16u * ((q >> 1) & 3);
+  }
+  int wrd[2];     // weight chunk this lane reads in step t
+  int ard[2][4];  // activation chunk this lane reads for MFMA j of step t
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    wrd[t] = 4 * col + ((2 * t + kh) ^ ((col >> 2) & 3));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ard[t][j] = WCH + (col < MP ? ((t * 4 + j) * 2 + kh) * MP + col : ACH);
+  }
 
   float c2v = 0.f, offset = 0.f;
   if constexpr (DQ) {
@@ -449,31 +465,34 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
     offset = sc.offset[0];
   }
 
-  struct WR {
-    uint4 p;
-    uint32_t q;
-    float s;
+  struct SR {
+    uint32_t q[2];
+    float s[2];
   };
-  WR wr[NB];
-  auto issue = [&](int64_t i, auto U) {  // step i of this wave into ring slot U
+  SR sr[NB];
+  auto issue = [&](int64_t i, auto U) {  // group i of this wave into ring slot U
     constexpr int u = decltype(U)::value;
-    const int64_t st = wave + i * KW;
-    wr[u].p = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, poff + (uint32_t)(32 * st), 0, 0));
-    const int64_t sl = st < nsteps ? st : nsteps - 1;
-    const int64_t b = (nc * K + 64 * sl) >> log2bs;  // one block per (column, step)
-    if constexpr (DQ) {
-      wr[u].q = sc.q[b];
-      wr[u].s = sc.absmax2[b >> sc.log2bs2];
-    } else {
-      wr[u].s = sc.absmax[b];
-    }
+    const int64_t g = g0 + i;
     uint4 *dst = slot(U);
 #pragma unroll
-    for (int d = 0; d < ND; ++d) load_lds16(ars, dst + 64 * d, goff[d] + (uint32_t)(128 * st));
+    for (int d = 0; d < WND; ++d) load_lds16(prs, dst + 64 * d, woff[d] + (uint32_t)(64 * g));
+#pragma unroll
+    for (int d = 0; d < AND; ++d) load_lds16(ars, dst + WCH + 64 * d, aoff[d] + (uint32_t)(256 * g));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t st = 2 * g + t;
+      const int64_t sl = st < nsteps ? st : nsteps - 1;
+      const int64_t b = (nc * K + 64 * sl) >> log2bs;  // one block per (column, step)
+      if constexpr (DQ) {
+        sr[u].q[t] = sc.q[b];
+        sr[u].s[t] = sc.absmax2[b >> sc.log2bs2];
+      } else {
+        sr[u].s[t] = sc.absmax[b];
+      }
+    }
   };
 
-  // prologue: steps 0 .. NB - 2 in flight while the tables are built
+  // prologue: groups 0 .. NB - 2 in flight while the tables are built
   static_for<NB - 1>([&](auto U) { issue(decltype(U)::value, U); });
   if (tid < 256) {
     lut[tid] = f32_to_bf16_rne(table.v[tid >> 4]) | (f32_to_bf16_rne(table.v[tid & 15]) << 16);
@@ -481,7 +500,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
   }
   if (lane < NB) {
     static_for<NB>([&](auto U) {
-      if (lane == decltype(U)::value) slot(U)[CH] = make_uint4(0, 0, 0, 0);
+      if (lane == decltype(U)::value) slot(U)[WCH + ACH] = make_uint4(0, 0, 0, 0);
     });
   }
   __syncthreads();
@@ -490,29 +509,34 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
 #pragma unroll
   for (int i = 0; i < RR; ++i) acc[i] = 0.f;
 
-  auto compute = [&](auto U) {
+  auto compute = [&](int64_t i, auto U) {
     constexpr int u = decltype(U)::value;
-    const WR &r = wr[u];
     const uint4 *sl = slot(U);
-    const uint32_t pw[4] = {r.p.x, r.p.y, r.p.z, r.p.w};
-    f32x16_t tile;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tile[i] = 0.f;
+    for (int t = 0; t < 2; ++t) {
+      if (2 * (g0 + i) + t < nsteps) {  // wave-uniform
+        const uint4 w = sl[wrd[t]];
+        const uint32_t pw[4] = {w.x, w.y, w.z, w.w};
+        f32x16_t tile;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t bw[4];
+        for (int e = 0; e < 16; ++e) tile[e] = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bw[q] = lut[(pw[j] >> (8 * q)) & 0xffu];
-      tile = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, sl[rd[j]]),
-                                                     __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3])),
-                                                     tile, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          uint32_t bw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bw[q] = lut[(pw[j] >> (8 * q)) & 0xffu];
+          tile = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, sl[ard[t][j]]),
+              __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3])), tile, 0, 0, 0);
+        }
+        const float a = DQ ? code2[sr[u].q[t]] * sr[u].s[t] + offset : sr[u].s[t];  // block scale
+#pragma unroll
+        for (int e = 0; e < RR; ++e) acc[e] = fmaf(a, tile[e], acc[e]);
+      }
     }
-    const float a = DQ ? code2[r.q] * r.s + offset : r.s;  // the block scale
-#pragma unroll
-    for (int i = 0; i < RR; ++i) acc[i] = fmaf(a, tile[i], acc[i]);
   };
 
-  // steady state: issue step i + NB - 1, wait for step i (the oldest in
+  // steady state: issue group i + NB - 1, wait for group i (the oldest in
   // flight: (NB - 1) * PER younger loads may stay outstanding), compute it
   constexpr int kWait = (NB - 1) * PER;
   const int64_t npad = (nw + NB - 1) / NB * NB;
@@ -524,7 +548,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8));
       asm volatile("" ::: "memory");
-      if (i < nw) compute(U);
+      if (i < nw) compute(i, U);
     });
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no LDS-direct load outlives the loop
@@ -532,16 +556,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
   // sum the waves' partial tiles (wave order) and store
   if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < RR; ++i) red[((wave - 1) * RR + i) * 64 + lane] = acc[i];
+    for (int e = 0; e < RR; ++e) red[((wave - 1) * RR + e) * 64 + lane] = acc[e];
   }
   __syncthreads();
   if (wave == 0 && n < N) {
 #pragma unroll
-    for (int i = 0; i < RR; ++i) {
-      float v = acc[i];
-      for (int w = 1; w < KW; ++w) v += red[((w - 1) * RR + i) * 64 + lane];
-      // accumulator layout: column = lane % 32, row = 8 (i / 4) + 4 (lane / 32) + i % 4
-      const int64_t m = 8 * (i >> 2) + 4 * kh + (i & 3);
+    for (int e = 0; e < RR; ++e) {
+      float v = acc[e];
+      for (int w = 1; w < KW; ++w) v += red[((w - 1) * RR + e) * 64 + lane];
+      // accumulator layout: column = lane % 32, row = 8 (e / 4) + 4 (lane / 32) + e % 4
+      const int64_t m = 8 * (e >> 2) + 4 * kh + (e & 3);
       if (m < M) store_elem<CDT>(C, m * N + n, v);
     }
   }
@@ -554,15 +578,14 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
   Table16f table;
   const uint32_t *bits = table_bits(qt);
   for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
-  if (M <= 32 && log2bs >= 6 && K % 64 == 0 && K < (1 << 23)) {  // narrow M
+  if (gemm_narrow_eligible(M, K, log2bs)) {  // narrow M
     const dim3 sgrid((unsigned)((N + 31) / 32));
 #define QMV_N(CDT, DQV, MPV, NBV, KWV)                                                          \
   hipLaunchKernelGGL((gemm_4bit_narrow_kernel<CDT, DQV, MPV, NBV, KWV>), sgrid, dim3(64 * KWV), 0, \
                      st, a, M, N, K, packed, sc, log2bs, table, C)
-#define QMV_NM(CDT, DQV)                           \
-  if (M <= 8) { QMV_N(CDT, DQV, 8, 4, 8); }        \
-  else if (M <= 16) { QMV_N(CDT, DQV, 16, 3, 8); } \
-  else { QMV_N(CDT, DQV, 32, 2, 4); }
+#define QMV_NM(CDT, DQV)                        \
+  if (M <= 8) { QMV_N(CDT, DQV, 8, 2, 4); }     \
+  else { QMV_N(CDT, DQV, 16, 2, 4); }
 #define QMV_ND(CDT) \
   if (dq) { QMV_NM(CDT, true); } else { QMV_NM(CDT, false); }
     if (c_dtype == kF32) { QMV_ND(kF32); }

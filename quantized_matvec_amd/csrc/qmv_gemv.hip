@@ -701,6 +701,10 @@ static hipError_t launch_lut(const void *x, int M, int64_t N, int64_t K, const u
 hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_t K,
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
                             void *y, int y_dtype, hipStream_t st) {
+  // 4 to 8 rows of bf16 activations: the MFMA kernel of gemm_4bit (the table
+  // kernel's dot products grow with M, the MFMA's do not)
+  if (x_dtype == kBF16 && M >= 4 && gemm_narrow_eligible(M, K, log2bs))
+    return launch_gemm_4bit(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
   if (x_dtype == kBF16) return launch_lut<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
   if (x_dtype == kF16) return launch_lut<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
   if (y_dtype == kF32) return launch_f32x<kF32>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);

@@ -173,13 +173,13 @@ def test_gemm_full_output(M, qt, dq):
     assert rel_l2(f64(Cf), ref) <= 1e-2
 
 
-@pytest.mark.parametrize("rows", [64, 200])
+@pytest.mark.parametrize("rows", [17, 32, 64, 200])
 @pytest.mark.parametrize("qt", ["nf4", "fp4"])
 def test_gemm_identity_rows_exact(qt, rows):
     """Rows of the identity pick rows of the bf16 dequantized weight; every
-    other product is an exact zero, so any order of summation is exact (64
-    rows run the split-K kernel, 200 rows the tile kernel: both multiply
-    bf16-rounded dequantized weights)."""
+    other product is an exact zero, so any order of summation is exact (17
+    to 64 rows run the split-K kernel, 200 rows the tile kernel: both
+    multiply bf16-rounded dequantized weights)."""
     N, K = 300, 256
     W = gaussian((N, K), 0.02, 9, "bf16")
     p_ref, a_ref = O.quantize_4bit(f64(W), 64, qt)
@@ -191,10 +191,10 @@ def test_gemm_identity_rows_exact(qt, rows):
     assert np.array_equal(got, What[:, :rows].T)
 
 
-@pytest.mark.parametrize("rows", [1, 8, 16, 20, 32])
+@pytest.mark.parametrize("rows", [1, 5, 8, 9, 16])
 @pytest.mark.parametrize("qt", ["nf4", "fp4"])
 def test_gemm_narrow_identity_rows_exact(qt, rows):
-    """Up to 32 rows and blocks of 64 or more take the narrow kernel, which
+    """Up to 16 rows and blocks of 64 or more take the narrow kernel, which
     multiplies bf16-rounded code values by the activations and applies the
     block scale per 64 k-values in fp32: a row of the identity then returns
     fp32(a_hat * bf16(T[code])) bit for bit (a zero of either sign reads +0,
