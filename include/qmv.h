@@ -88,7 +88,7 @@ int qmv_quantize_4bit(const void *W, qmv_dtype w_dtype, int64_t numel, int32_t b
                       qmv_quant_type quant_type, uint8_t *packed, float *absmax, void *stream);
 
 /* Bytes of device workspace qmv_double_quant needs for ``nblocks`` scales
- * (the partial sums of the mean). */
+ * (the partial sums of the mean and the exponent bounds of their inputs). */
 size_t qmv_double_quant_workspace(int64_t nblocks);
 
 /*

@@ -385,10 +385,18 @@ hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int l
 //
 // 1. The mean of the scales: float64 sums over consecutive runs of 256 in a
 //    fixed order, level after level, until one value S is left; offset =
-//    fp32(S / nblocks).  The order is part of the contract, so every run is a
-//    plain sequential loop in one thread.  Every workgroup of the first
-//    launch sums 16 runs of the first level; one workgroup then sums the
-//    remaining (few) levels and writes the offset.
+//    fp32(S / nblocks).  The order is part of the contract, but a float64
+//    sum of fp32 values is exact, and then independent of the order, when
+//    all its partial sums are integer multiples of the smallest ulp u among
+//    the values and below 2^53 u: for k values below 2^h with ulp >= 2^l
+//    that holds when log2(k) + h - l <= 53.  So every workgroup of the first
+//    launch takes 16 runs of the first level and, when its values pass that
+//    test for k = 256, sums each run as a wave reduction, otherwise as the
+//    plain sequential loop; it also records h and l.  The encode launch then
+//    combines the first-level sums: if all n values pass the test (log2 n in
+//    place of log2 256) any order gives the tree's exact sum, else it runs
+//    the remaining levels in tree order.  Beyond 4096 first-level runs one
+//    workgroup of a third launch sums the remaining levels in tree order.
 // 2. Per group of blocksize2 scales: c = fp32(a - offset), s = max |c|, and
 //    the code of c / s is the rank of c among the exact float64 thresholds
 //    s * mid[j] of the (strictly increasing) 256-entry table; ties go toward
@@ -443,14 +451,87 @@ __device__ __forceinline__ void sum_runs16(const In *__restrict__ in, int64_t n,
   __syncthreads();  // stage is reused
 }
 
-// First level: workgroup g sums runs [16 g, 16 g + 16) of the scales.  When
-// that level is already a single run it also writes the offset.
+// Exponent bounds of an fp32 value for the exactness test: |v| < 2^h and
+// ulp(v) >= 2^l.  Zero contributes nothing (h = -1000, l = +1000); inf and
+// NaN fail the test (h = +1000).
+__device__ __forceinline__ void exp_bounds(float v, int &h, int &l) {
+  const uint32_t e = (__builtin_bit_cast(uint32_t, v) >> 23) & 255u;
+  const bool zero = (__builtin_bit_cast(uint32_t, v) & 0x7fffffffu) == 0u;
+  h = zero ? -1000 : (e == 255u ? 1000 : (e == 0u ? -126 : (int)e - 126));
+  l = zero ? 1000 : (e == 0u ? -149 : (int)e - 150);
+}
+
+// First level: workgroup g sums runs [16 g, 16 g + 16) of the scales and
+// stores (max h, min l) of its values in stats[g].  When that level is
+// already a single run it also writes the offset.
 __global__ __launch_bounds__(256) void dq_sum_kernel(const float *__restrict__ absmax, int64_t n,
                                                      double *__restrict__ levels,
+                                                     int2 *__restrict__ stats,
                                                      float *__restrict__ offset) {
   __shared__ double stage[kSumRuns * (kFanIn + 1)];
-  sum_runs16<float>(absmax, n, blockIdx.x, levels, stage);
-  if (n <= kFanIn && threadIdx.x == 0) offset[0] = (float)__ddiv_rn(levels[0], (double)n);
+  __shared__ int wh[4], wl[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t g = blockIdx.x;
+  const int64_t nout = (n + kFanIn - 1) / kFanIn;
+  const int64_t run0 = g * kSumRuns;
+  const int64_t base = run0 * kFanIn;
+  const int64_t rem = n - base;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(absmax + base, (uint32_t)((rem < kSumRuns * kFanIn ? rem : kSumRuns * kFanIn) * 4));
+  float v[kSumRuns];
+#pragma unroll
+  for (int i = 0; i < kSumRuns; ++i)  // element base + i * 256 + tid (zero past n)
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         rs, (uint32_t)((i * kFanIn + tid) * 4), 0, 0));
+  int h = -1000, l = 1000;
+#pragma unroll
+  for (int i = 0; i < kSumRuns; ++i) {
+    int hi, li;
+    exp_bounds(v[i], hi, li);
+    h = max(h, hi);
+    l = min(l, li);
+    stage[i * (kFanIn + 1) + tid] = (double)v[i];
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    h = max(h, __shfl_xor(h, o));
+    l = min(l, __shfl_xor(l, o));
+  }
+  if (lane == 0) {
+    wh[wave] = h;
+    wl[wave] = l;
+  }
+  __syncthreads();
+  h = max(max(wh[0], wh[1]), max(wh[2], wh[3]));
+  l = min(min(wl[0], wl[1]), min(wl[2], wl[3]));
+  if (tid == 0) stats[g] = make_int2(h, l);
+  if (8 + h - l <= 53) {
+    // exact: wave w sums runs 4 w .. 4 w + 3, lane l adds values 4 l .. 4 l + 3
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int run = 4 * wave + r;
+      const double *row = stage + run * (kFanIn + 1) + 4 * lane;
+      double t = (row[0] + row[1]) + (row[2] + row[3]);
+      for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+      if (lane == 0 && run0 + run < nout) levels[run0 + run] = t;
+    }
+  } else if (tid < kSumRuns && run0 + tid < nout) {
+    const double *row = stage + tid * (kFanIn + 1);
+    double t = 0.0;
+    for (int k0 = 0; k0 < kFanIn; k0 += 32) {
+      double w[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) w[k] = row[k0 + k];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) t = __dadd_rn(t, w[k]);  // + 0 past n: unchanged
+    }
+    levels[run0 + tid] = t;
+  }
+  if (n <= kFanIn) {  // one run: its sum is S
+    __syncthreads();
+    if (tid == 0) offset[0] = (float)__ddiv_rn(levels[0], (double)n);
+  }
 }
 
 // The remaining levels, in one workgroup (a kernel boundary separates it from
@@ -472,27 +553,114 @@ __global__ __launch_bounds__(256) void dq_top_kernel(double *__restrict__ levels
 // Encode: a workgroup takes a tile of 256 * E consecutive scales, E per
 // thread (E = 8, or 16 when a group of 4096 would span more than 256
 // threads); the G = blocksize2 / E threads of a group reduce max |c|.
+//
+// With 1 < nl <= kTopFused first-level sums every workgroup first derives
+// the offset from them (the same bits in every workgroup; workgroup 0 writes
+// them); otherwise an earlier launch wrote it.
+constexpr int kTopFused = 4096;
+
+__device__ __forceinline__ float fused_offset(const double *__restrict__ levels, int64_t nl,
+                                              const int2 *__restrict__ stats, int64_t n, double *red) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // the first-level sums this thread may need (levels tid + 256 k), all in flight
+  constexpr int kPer = kTopFused / 256;
+  double v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int64_t i = tid + 256 * k;
+    v[k] = i < nl ? levels[i] : 0.0;
+  }
+  // exactness over all n values: combine the first launch's per-workgroup bounds
+  const int64_t nst = (nl + kSumRuns - 1) / kSumRuns;  // <= 256
+  int h = -1000, l = 1000;
+  for (int64_t i = tid; i < nst; i += 256) {
+    const int2 st = stats[i];
+    h = max(h, st.x);
+    l = min(l, st.y);
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    h = max(h, __shfl_xor(h, o));
+    l = min(l, __shfl_xor(l, o));
+  }
+  int *ri = reinterpret_cast<int *>(red);
+  if (lane == 0) {
+    ri[2 * wave] = h;
+    ri[2 * wave + 1] = l;
+  }
+  __syncthreads();
+  h = max(max(ri[0], ri[2]), max(ri[4], ri[6]));
+  l = min(min(ri[1], ri[3]), min(ri[5], ri[7]));
+  int log2n = 0;
+  while (((int64_t)1 << log2n) < n) ++log2n;
+  __syncthreads();
+  double total;
+  if (log2n + h - l <= 53) {
+    // exact: any order
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) t += v[k];
+    for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+    if (lane == 0) red[wave] = t;
+    __syncthreads();
+    total = (red[0] + red[1]) + (red[2] + red[3]);
+  } else {
+    // the remaining levels in tree order: <= 16 runs, then one; thread r
+    // reads run r 32 values at a time (all in flight), adding +0 past nl
+    const int64_t nn = (nl + kFanIn - 1) / kFanIn;
+    if (tid < nn) {
+      const double *row = levels + (int64_t)tid * kFanIn;
+      const int64_t len = nl - (int64_t)tid * kFanIn < kFanIn ? nl - (int64_t)tid * kFanIn : kFanIn;
+      double t = 0.0;
+      for (int64_t k0 = 0; k0 < len; k0 += 32) {
+        double w[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) w[k] = k0 + k < len ? row[k0 + k] : 0.0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) t = __dadd_rn(t, w[k]);
+      }
+      red[tid] = t;
+    }
+    __syncthreads();
+    total = red[0];
+    if (nn > 1) {
+      total = 0.0;
+      for (int64_t r = 0; r < nn; ++r) total = __dadd_rn(total, red[r]);
+    }
+  }
+  return (float)__ddiv_rn(total, (double)n);
+}
+
 template <int E>
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict__ absmax,
                                                         int64_t n, int log2bs2, Code2Table code2,
-                                                        int linear,
-                                                        const float *__restrict__ offset,
+                                                        int linear, const double *__restrict__ levels,
+                                                        const int2 *__restrict__ stats, int64_t nl,
+                                                        float *__restrict__ offset,
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ absmax2,
                                                         float *__restrict__ code2_out) {
   __shared__ double mid[256];
   __shared__ float wave_max[4];
+  __shared__ double red[kTopFused / kFanIn];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (tid < 255) mid[tid] = ((double)code2.v[tid] + (double)code2.v[tid + 1]) * 0.5;  // exact
   if (blockIdx.x == 0) code2_out[tid] = code2.v[tid];
+  float off;
+  if (nl > 1 && nl <= kTopFused) {
+    off = fused_offset(levels, nl, stats, n, red);
+    if (blockIdx.x == 0 && tid == 0) offset[0] = off;
+  } else {
+    off = offset[0];  // written by an earlier launch
+  }
   __syncthreads();
 
   const int G = (1 << log2bs2) / E;  // threads per group: 2 .. 256
   const int64_t tile = (int64_t)256 * E;
   const int64_t ntiles = (n + tile - 1) / tile;
-  const float off = offset[0];
 
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t i0 = t * tile + (int64_t)tid * E;
@@ -574,7 +742,8 @@ size_t double_quant_workspace_bytes(int64_t nblocks) {
     n = (n + kFanIn - 1) / kFanIn;
     total += (size_t)n * sizeof(double);
   } while (n > 1);
-  return total;
+  const int64_t runs = (nblocks + kFanIn - 1) / kFanIn;
+  return total + (size_t)((runs + kSumRuns - 1) / kSumRuns) * sizeof(int2);  // + exponent bounds
 }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,
@@ -582,11 +751,18 @@ hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2
                                float *offset, float *code2_out, void *ws, hipStream_t st) {
   double *levels = static_cast<double *>(ws);
   const int64_t runs = (nblocks + kFanIn - 1) / kFanIn;
+  size_t lv = 0;  // doubles in all levels
+  for (int64_t m = nblocks; m > 1 || lv == 0;) {
+    m = (m + kFanIn - 1) / kFanIn;
+    lv += (size_t)m;
+    if (m <= 1) break;
+  }
+  int2 *stats = reinterpret_cast<int2 *>(levels + lv);
   hipLaunchKernelGGL(dq_sum_kernel, dim3((unsigned)((runs + kSumRuns - 1) / kSumRuns)), dim3(256), 0,
-                     st, absmax, nblocks, levels, offset);
+                     st, absmax, nblocks, levels, stats, offset);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (runs > 1) {
+  if (runs > kTopFused) {  // else the encode launch combines the first level itself
     hipLaunchKernelGGL(dq_top_kernel, dim3(1), dim3(256), 0, st, levels, runs, nblocks, offset);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -597,7 +773,8 @@ hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
 #define QMV_E(EV)                                                                          \
   hipLaunchKernelGGL(dq_encode_kernel<EV>, dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
-                     code2, linear ? 1 : 0, offset, q, absmax2, code2_out)
+                     code2, linear ? 1 : 0, levels, stats, runs > kTopFused ? (int64_t)1 : runs, \
+                     offset, q, absmax2, code2_out)
   if (E == 8) QMV_E(8); else QMV_E(16);
 #undef QMV_E
   return hipGetLastError();

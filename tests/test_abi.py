@@ -70,7 +70,7 @@ def test_quantize_preconditions(qmvlib):
 def test_double_quant_preconditions(qmvlib):
     f = qmvlib.qmv_double_quant
     ws = qmvlib.qmv_double_quant_workspace(1000)
-    assert ws == 8 * (4 + 1)      # level sums: 4 runs, then 1
+    assert ws == 8 * (4 + 1) + 8  # level sums (4 runs, then 1), one exponent-bound pair
     assert qmvlib.qmv_double_quant_workspace(0) == 0
     args = lambda **k: dict(dict(a=P, n=1000, bs2=256, code=None, q=P, a2=P, off=P, c2o=P, w=P2, wsb=ws), **k)
     call = lambda d: f(d["a"], d["n"], d["bs2"], d["code"], d["q"], d["a2"], d["off"], d["c2o"], d["w"], d["wsb"], None)

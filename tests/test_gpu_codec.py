@@ -121,9 +121,30 @@ def dq_case(n, bs2, seed, code2=None):
     return q, a2, off, c2
 
 
-@pytest.mark.parametrize("n", [1, 2, 255, 256, 257, 4096, 65537, 70001])
+@pytest.mark.parametrize("n", [1, 2, 255, 256, 257, 4096, 65537, 70001, 256 * 4096,
+                               256 * 4096 + 1])
 def test_double_quant_bitexact_sizes(n):
+    """Up to 4096 first-level runs the encode launch combines the runs; the
+    last size takes the separate top-level launch."""
     dq_case(n, 256, seed=n)
+
+
+@pytest.mark.parametrize("n", [5000, 70001])
+def test_double_quant_mean_wide_exponents(n):
+    """Scales whose exponents span too far for an exact float64 sum: the
+    partial sums round, so only the fixed tree order gives the oracle's mean
+    (both the first-level runs and the levels above take the ordered path)."""
+    rng = np.random.default_rng(n)
+    a = (np.abs(rng.standard_normal(n)) * 0.02).astype(np.float32)
+    a[::97] = np.float32(3e-30)
+    a[5] = np.float32(7e9)
+    ag = torch.from_numpy(a).cuda()
+    q, a2, off, c2 = qmv.double_quant(ag, 256)
+    torch.cuda.synchronize()
+    q_ref, a2_ref, off_ref = O.double_quant(a, 256)
+    assert bits32(off.cpu().numpy())[0] == bits32([off_ref])[0]
+    assert np.array_equal(bits32(a2.cpu().numpy()), bits32(a2_ref))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
 @pytest.mark.parametrize("bs2", [32, 64, 512, 4096])
