@@ -20,27 +20,33 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// Tile: 128 (M) x 128 (N) x 64 (K); 4 waves as 2 x 2, each 64 x 64 as 2 x 2
-// accumulators of v_mfma_f32_32x32x16_bf16.  LDS rows are padded to 72 bf16
-// (144 bytes) so that the 32 rows an operand read touches fall in different
-// banks.  Two LDS stages: while the matrix cores consume stage k, the global
-// loads of tile k + 1 are in flight, and they are dequantized into the other
-// stage afterwards (one barrier per k-tile).
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLd = kBK + 8;                    // padded row, bf16 elements
-constexpr int kStage = (kBM + kBN) * kLd;       // bf16 elements per stage
+// Tile: 128 (M) x BN (N, 128 or 64) x 64 (K); 4 waves as 2 x 2, each 64 x
+// BN / 2 as 2 x BN / 64 accumulators of v_mfma_f32_32x32x16_bf16.  LDS rows
+// are padded to 72 bf16 (144 bytes) so that the 32 rows an operand read
+// touches fall in different banks.  Two LDS stages: while the matrix cores
+// consume stage k, the global loads of tile k + 1 are in flight, and they
+// are dequantized into the other stage afterwards (one barrier per k-tile).
+// BN = 64 doubles the workgroups for row counts whose 128-wide tiles would
+// leave compute units idle.
+constexpr int kBM = 128, kBK = 64;
+constexpr int kLd = kBK + 8;  // padded row, bf16 elements
 
 struct Table16f {
   float v[16];
 };
 
-template <int CDT, bool DQ>
+template <int CDT, bool DQ, int BN>
 __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__restrict__ A, int64_t M,
                                                            int64_t N, int64_t K,
                                                            const uint8_t *__restrict__ packed,
                                                            Scales sc, int log2bs, Table16f table,
                                                            void *__restrict__ Cv) {
+  constexpr int kStage = (kBM + BN) * kLd;  // bf16 elements per stage
+  constexpr int NJ = BN / 64;               // 32-column accumulators per wave
+  constexpr int BPT = BN / 4;               // weights per thread and tile: 32 or 16
+  constexpr int TPR = kBK / BPT;            // threads per weight row: 2 or 4
   using CT = typename Storage<CDT>::type;
+  using PW = typename std::conditional<BPT == 32, uint4, uint2>::type;  // packed bytes per thread
   CT *C = static_cast<CT *>(Cv);
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
   __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
@@ -50,68 +56,70 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t KT = (K + kBK - 1) / kBK;
   const bool k_tail = (K % kBK) != 0;  // last tile has 32 of 64 columns
 
   // loader roles: thread t moves row t / 2, columns [32 (t % 2), +32) of the
-  // A tile and of the weight tile
+  // A tile, and row t / TPR, columns [BPT (t % TPR), +BPT) of the weight tile
   const int lr = tid >> 1, lh = tid & 1;
+  const int br = tid / TPR, bq = tid % TPR;
   const int64_t arow = m0 + lr < M ? m0 + lr : M - 1;  // rows past M are never stored
-  const int64_t brow = n0 + lr < N ? n0 + lr : N - 1;  // columns past N likewise
+  const int64_t brow = n0 + br < N ? n0 + br : N - 1;  // columns past N likewise
   // two register sets: tile k + 2 is loaded while tile k is multiplied and
   // tile k + 1 (loaded an iteration earlier) is staged
   uint4 ra_[2][4];
-  uint4 rb_[2];
+  PW rb_[2];
   float rsa_[2];
   uint32_t rsq_[2];
   auto load_tile = [&](int64_t kt, auto slot_tag) {
     constexpr int SL = decltype(slot_tag)::value;
     uint4(&ra)[4] = ra_[SL];
-    uint4 &rb = rb_[SL];
-    float &rsa = rsa_[SL];
-    uint32_t &rsq = rsq_[SL];
     int64_t k = kt * kBK + 32 * lh;
     if (k >= K) k = K - 32;  // the missing half of a tail tile (zeroed when staged)
     const uint4 *ap = reinterpret_cast<const uint4 *>(A + arow * K + k);
 #pragma unroll
     for (int q = 0; q < 4; ++q) ra[q] = ap[q];
-    const int64_t e0 = brow * K + k;
-    rb = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
+    int64_t kb = kt * kBK + BPT * bq;
+    if (kb >= K) kb = K - BPT;  // likewise
+    const int64_t e0 = brow * K + kb;
+    rb_[SL] = *reinterpret_cast<const PW *>(packed + (e0 >> 1));
     const int64_t b = e0 >> log2bs;
     if constexpr (DQ) {
-      rsq = sc.q[b];
-      rsa = sc.absmax2[b >> sc.log2bs2];
+      rsq_[SL] = sc.q[b];
+      rsa_[SL] = sc.absmax2[b >> sc.log2bs2];
     } else {
-      rsa = sc.absmax[b];
+      rsa_[SL] = sc.absmax[b];
     }
   };
   auto stage_tile = [&](int64_t kt, int buf, auto slot_tag) {
     constexpr int SL = decltype(slot_tag)::value;
     const uint4(&ra)[4] = ra_[SL];
-    const uint4 &rb = rb_[SL];
     const float rsa = rsa_[SL];
     const uint32_t rsq = rsq_[SL];
     (void)rsq;
     uint16_t *As = smem + buf * kStage;
     uint16_t *Bs = As + kBM * kLd;
-    const bool zero = k_tail && kt == KT - 1 && lh == 1;
+    const bool last = k_tail && kt == KT - 1;
+    const bool zero_a = last && lh == 1;
     uint4 *ad = reinterpret_cast<uint4 *>(As + lr * kLd + 32 * lh);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ad[q] = zero ? make_uint4(0, 0, 0, 0) : ra[q];
-    const float a = zero ? 0.f : (DQ ? code2[rsq] * rsa + sc_offset(sc) : rsa);
-    const uint32_t pw[4] = {rb.x, rb.y, rb.z, rb.w};
-    uint32_t o[16];
+    for (int q = 0; q < 4; ++q) ad[q] = zero_a ? make_uint4(0, 0, 0, 0) : ra[q];
+    const bool zero_b = last && BPT * bq >= 32;
+    const float a = zero_b ? 0.f : (DQ ? code2[rsq] * rsa + sc_offset(sc) : rsa);
+    uint32_t pw[BPT / 8];
+    __builtin_memcpy(pw, &rb_[SL], sizeof(pw));
+    uint32_t o[BPT / 2];
 #pragma unroll
-    for (int bb = 0; bb < 16; ++bb) {
+    for (int bb = 0; bb < BPT / 2; ++bb) {
       const float2 t = lut2[(pw[bb >> 2] >> (8 * (bb & 3))) & 0xffu];
       // dequantized weights: fp32(T * a_hat) rounded to bf16 (nearest even)
       const f32x2_t v = {materialize(t.x * a), materialize(t.y * a)};
       o[bb] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
     }
-    uint4 *bd = reinterpret_cast<uint4 *>(Bs + lr * kLd + 32 * lh);
+    uint4 *bd = reinterpret_cast<uint4 *>(Bs + br * kLd + BPT * bq);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    for (int q = 0; q < BPT / 8; ++q) bd[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
   };
 
   using S0 = std::integral_constant<int, 0>;
@@ -124,11 +132,11 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
   stage_tile(0, 0, S0{});
   __syncthreads();
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -137,21 +145,21 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
     const uint16_t *Bs = As + kBM * kLd;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t af[2], bfr[2];
+      bf16x8_t af[2], bfr[NJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm * 64 + i * 32 + (lane & 31);
         af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * kLd + ks * 16 + (lane >> 5) * 8);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + j * 32 + (lane & 31);
+      for (int j = 0; j < NJ; ++j) {
+        const int col = wn * (BN / 2) + j * 32 + (lane & 31);
         bfr[j] = *reinterpret_cast<const bf16x8_t *>(Bs + col * kLd + ks * 16 + (lane >> 5) * 8);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -178,8 +186,8 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -613,16 +621,22 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
 #undef QMV_S
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-#define QMV_M(CDT, DQV)                                                                        \
-  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV>), grid, dim3(256), 0, st, a, M, N, K, packed, \
+  // 128-wide weight tiles unless they would leave compute units idle
+  const int64_t mt = (M + kBM - 1) / kBM;
+  const bool wide = ((N + 127) / 128) * mt >= (int64_t)device_cu_count();
+  const dim3 grid((unsigned)(wide ? (N + 127) / 128 : (N + 63) / 64), (unsigned)mt);
+#define QMV_M(CDT, DQV, BNV)                                                                    \
+  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV, BNV>), grid, dim3(256), 0, st, a, M, N, K, packed, \
                      sc, log2bs, table, C)
+#define QMV_MB(CDT, DQV) \
+  if (wide) { QMV_M(CDT, DQV, 128); } else { QMV_M(CDT, DQV, 64); }
 #define QMV_MD(CDT) \
-  if (dq) { QMV_M(CDT, true); } else { QMV_M(CDT, false); }
+  if (dq) { QMV_MB(CDT, true); } else { QMV_MB(CDT, false); }
   if (c_dtype == kF32) { QMV_MD(kF32); }
   else if (c_dtype == kF16) { QMV_MD(kF16); }
   else { QMV_MD(kBF16); }
 #undef QMV_MD
+#undef QMV_MB
 #undef QMV_M
   return hipGetLastError();
 }

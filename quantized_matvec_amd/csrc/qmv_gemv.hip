@@ -600,7 +600,7 @@ static Table16 host_table16(int qt, int dt) {
 }
 
 // Compute units of the current device (cached per device).
-static int cu_count() {
+int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -619,7 +619,7 @@ static hipError_t launch_lut_m(const void *x, int64_t N, int64_t K, const uint8_
                                hipStream_t st) {
   constexpr int kGemvThreads = LutShape<M>::kThreads;
   const int64_t waves_per_wg = kGemvThreads / 64;
-  int64_t grid = (int64_t)cu_count() * LutShape<M>::kWgPerCu;
+  int64_t grid = (int64_t)device_cu_count() * LutShape<M>::kWgPerCu;
   grid = std::min<int64_t>(grid, (N + waves_per_wg - 1) / waves_per_wg);
   const int64_t total_waves = grid * waves_per_wg;
   const int rpw = (int)(N / total_waves), rem = (int)(N % total_waves);
@@ -641,7 +641,7 @@ static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *
                             const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
                             hipStream_t st) {
   const int64_t waves_per_wg = kM1Threads / 64;
-  int64_t grid = (int64_t)cu_count();
+  int64_t grid = (int64_t)device_cu_count();
   grid = std::min<int64_t>(grid, (N + waves_per_wg - 1) / waves_per_wg);
   const int64_t total_waves = grid * waves_per_wg;
   const int rpw = (int)(N / total_waves), rem = (int)(N % total_waves);

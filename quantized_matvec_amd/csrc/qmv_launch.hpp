@@ -45,6 +45,9 @@ hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
                             void *y, int y_dtype, hipStream_t st);
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // True when gemm_4bit takes its narrow kernel: M <= 16 rows, blocks of 64 or
 // more, K a multiple of 64 (below 2^23).
 inline bool gemm_narrow_eligible(int64_t M, int64_t K, int log2bs) {
