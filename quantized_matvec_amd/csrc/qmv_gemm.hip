@@ -20,31 +20,35 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// Tile: 128 (M) x BN (N, 128 or 64) x 64 (K); 4 waves as 2 x 2, each 64 x
-// BN / 2 as 2 x BN / 64 accumulators of v_mfma_f32_32x32x16_bf16.  LDS rows
-// are padded to 72 bf16 (144 bytes) so that the 32 rows an operand read
-// touches fall in different banks.  Two LDS stages: while the matrix cores
-// consume stage k, the global loads of tile k + 1 are in flight, and they
-// are dequantized into the other stage afterwards (one barrier per k-tile).
-// BN = 64 doubles the workgroups for row counts whose 128-wide tiles would
-// leave compute units idle.
-constexpr int kBM = 128, kBK = 64;
+// Tile: BM (M, 128 or 256) x BN (N, 128 or 64) x 64 (K) for NT = 2 BM
+// threads; the waves form (BM / 64) x WN, each computing 64 x BN / WN as
+// 2 x NJ accumulators of v_mfma_f32_32x32x16_bf16.  LDS rows are padded to
+// 72 bf16 (144 bytes) so that the 32 rows an operand read touches fall in
+// different banks.  Two LDS stages: while the matrix cores consume stage k,
+// the global loads of tile k + 1 are in flight, and they are dequantized
+// into the other stage afterwards (one barrier per k-tile).  BN = 64 doubles
+// the workgroups for row counts whose 128-wide tiles would leave compute
+// units idle; BM = 256 halves how often a weight tile is dequantized.
+constexpr int kBK = 64;
 constexpr int kLd = kBK + 8;  // padded row, bf16 elements
 
 struct Table16f {
   float v[16];
 };
 
-template <int CDT, bool DQ, int BN>
-__global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__restrict__ A, int64_t M,
+template <int CDT, bool DQ, int BM, int BN>
+__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(const uint16_t *__restrict__ A, int64_t M,
                                                            int64_t N, int64_t K,
                                                            const uint8_t *__restrict__ packed,
                                                            Scales sc, int log2bs, Table16f table,
                                                            void *__restrict__ Cv) {
-  constexpr int kStage = (kBM + BN) * kLd;  // bf16 elements per stage
-  constexpr int NJ = BN / 64;               // 32-column accumulators per wave
-  constexpr int BPT = BN / 4;               // weights per thread and tile: 32 or 16
+  constexpr int NT = 2 * BM;                // threads
+  constexpr int kStage = (BM + BN) * kLd;   // bf16 elements per stage
+  constexpr int WN = NT / 64 / (BM / 64);   // waves along N (2)
+  constexpr int NJ = BN / WN / 32;          // 32-column accumulators per wave
+  constexpr int BPT = BN * kBK / NT;        // weights per thread and tile: 32 or 16
   constexpr int TPR = kBK / BPT;            // threads per weight row: 2 or 4
+  static_assert(NJ >= 1 && (BPT == 32 || BPT == 16), "tile shape");
   using CT = typename Storage<CDT>::type;
   using PW = typename std::conditional<BPT == 32, uint4, uint2>::type;  // packed bytes per thread
   CT *C = static_cast<CT *>(Cv);
@@ -54,8 +58,8 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t KT = (K + kBK - 1) / kBK;
   const bool k_tail = (K % kBK) != 0;  // last tile has 32 of 64 columns
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
     const uint32_t rsq = rsq_[SL];
     (void)rsq;
     uint16_t *As = smem + buf * kStage;
-    uint16_t *Bs = As + kBM * kLd;
+    uint16_t *Bs = As + BM * kLd;
     const bool last = k_tail && kt == KT - 1;
     const bool zero_a = last && lh == 1;
     uint4 *ad = reinterpret_cast<uint4 *>(As + lr * kLd + 32 * lh);
@@ -126,8 +130,10 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
   using S1 = std::integral_constant<int, 1>;
   load_tile(0, S0{});
   load_tile(KT > 1 ? 1 : 0, S1{});
-  lut2[tid] = make_float2(table.v[tid >> 4], table.v[tid & 15]);
-  if constexpr (DQ) code2[tid] = sc.code2[tid];
+  if (tid < 256) {
+    lut2[tid] = make_float2(table.v[tid >> 4], table.v[tid & 15]);
+    if constexpr (DQ) code2[tid] = sc.code2[tid];
+  }
   __syncthreads();
   stage_tile(0, 0, S0{});
   __syncthreads();
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
 
   auto mma_tile = [&](int buf) {
     const uint16_t *As = smem + buf * kStage;
-    const uint16_t *Bs = As + kBM * kLd;
+    const uint16_t *Bs = As + BM * kLd;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       bf16x8_t af[2], bfr[NJ];
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int col = wn * (BN / 2) + j * 32 + (lane & 31);
+        const int col = wn * (BN / WN) + j * 32 + (lane & 31);
         bfr[j] = *reinterpret_cast<const bf16x8_t *>(Bs + col * kLd + ks * 16 + (lane >> 5) * 8);
       }
 #pragma unroll
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_kernel(const uint16_t *__res
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int64_t col = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+      const int64_t col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -621,15 +627,20 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
 #undef QMV_S
     return hipGetLastError();
   }
-  // 128-wide weight tiles unless they would leave compute units idle
-  const int64_t mt = (M + kBM - 1) / kBM;
-  const bool wide = ((N + 127) / 128) * mt >= (int64_t)device_cu_count();
-  const dim3 grid((unsigned)(wide ? (N + 127) / 128 : (N + 63) / 64), (unsigned)mt);
-#define QMV_M(CDT, DQV, BNV)                                                                    \
-  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV, BNV>), grid, dim3(256), 0, st, a, M, N, K, packed, \
-                     sc, log2bs, table, C)
-#define QMV_MB(CDT, DQV) \
-  if (wide) { QMV_M(CDT, DQV, 128); } else { QMV_M(CDT, DQV, 64); }
+  // 256 x 128 tiles when they still give a workgroup to most compute units,
+  // else 128 x 128, else 128 x 64 (narrower tiles, more workgroups)
+  const int64_t cus = device_cu_count();
+  const int64_t nt128 = (N + 127) / 128;
+  const int shape = nt128 * ((M + 255) / 256) >= cus * 3 / 4 ? 2 : (nt128 * ((M + 127) / 128) >= cus ? 1 : 0);
+  const dim3 grid((unsigned)(shape ? nt128 : (N + 63) / 64),
+                  (unsigned)(shape == 2 ? (M + 255) / 256 : (M + 127) / 128));
+#define QMV_M(CDT, DQV, BMV, BNV)                                                                    \
+  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV, BMV, BNV>), grid, dim3(2 * BMV), 0, st, a, M, N, K, \
+                     packed, sc, log2bs, table, C)
+#define QMV_MB(CDT, DQV)                                     \
+  if (shape == 2) { QMV_M(CDT, DQV, 256, 128); }             \
+  else if (shape == 1) { QMV_M(CDT, DQV, 128, 128); }        \
+  else { QMV_M(CDT, DQV, 128, 64); }
 #define QMV_MD(CDT) \
   if (dq) { QMV_MB(CDT, true); } else { QMV_MB(CDT, false); }
   if (c_dtype == kF32) { QMV_MD(kF32); }
