@@ -134,7 +134,7 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
 constexpr int kQBins = 64;
 struct QuantArgs {
   Midpoints4 mids;
-  uint8_t cand[kQBins];  // J(b)
+  uint8_t cand[256];     // J(b); bins 64 .. 255 (clamped) count every midpoint
   float bin_scale;       // S
   float bin_offset;      // O
 };
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   // only after every thread has passed the next tile's barrier
   __shared__ float wave_max[2][4];
   __shared__ float thr[2][256 * E / 32 * TS];  // up to tile / 32 blocks per tile
-  __shared__ uint8_t cand[kQBins];  // bytes: the bin is the address
+  __shared__ uint8_t cand[256];  // bytes: the bin is the address
   __shared__ double mids[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
   const int blk_in_tile = tid / G;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
-  if (tid < kQBins) cand[tid] = qa.cand[tid];
+  cand[tid] = qa.cand[tid];
   if (tid < NT) mids[tid] = qa.mids.mid[tid];
   __syncthreads();
 
@@ -233,13 +233,30 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
     // normal (only the candidate uses n); an all-zero block has n = 0
     const float sc = m < 0x1p-100f ? 0x1p100f : (m > 0x1p100f ? 0x1p-100f : 1.f);
     const float inv = m > 0.f ? qa.bin_scale * __builtin_amdgcn_rcpf(m * sc) : 0.f;
+    // in phases, so that the 16 table reads of a phase are in flight together.
+    // bin = floor(S n + O), except within 1/256 below an integer where it is
+    // that integer (harmless: no midpoint lies within 0.02 of a bin edge),
+    // clamped to 0 .. 255 by the conversion: v_cvt_pk_u8_f32 rounds
+    // S n + O - 1/2 + 1/256 to the nearest integer and saturates
+    const float off = qa.bin_offset - 0.5f + 0x1p-8f;  // exact
+    int cb[E];
+    if (__builtin_amdgcn_ballot_w64(sc != 1.f) == 0) {  // wave-uniform: no rescaled block
+#pragma unroll
+      for (int i = 0; i < E; ++i) cb[i] = (int)__builtin_amdgcn_cvt_pk_u8_f32(fmaf(v[i], inv, off), 0, 0u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        cb[i] = (int)__builtin_amdgcn_cvt_pk_u8_f32(fmaf(v[i] * sc, inv, off), 0, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) cb[i] = (int)cand[cb[i]];
+    float tb[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) tb[i] = bt[1 + cb[i]];
     uint32_t code[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      int bin = (int)fmaf(v[i] * sc, inv, qa.bin_offset);  // S n + O
-      bin = bin < 0 ? 0 : (bin > kQBins - 1 ? kQBins - 1 : bin);
-      const int c = (int)cand[bin];
-      const int r = c + (v[i] > bt[1 + c] ? 1 : 0);
+      const int r = cb[i] + (v[i] > tb[i] ? 1 : 0);
       code[i] = (FULL || e0 + i < numel) ? rank_to_code<QT>(r) : 0u;
     }
 
@@ -334,7 +351,7 @@ static bool bin_geometry(const Midpoints4 &m, int nt, QuantArgs &qa) {
     }
   }
   if (best < 0.02) return false;
-  for (int b = 0; b < kQBins; ++b) {
+  for (int b = 0; b < 256; ++b) {
     int c = 0;
     for (int j = 0; j < nt; ++j)
       c += std::floor((double)qa.bin_scale * m.mid[j] + (double)qa.bin_offset) < b ? 1 : 0;
