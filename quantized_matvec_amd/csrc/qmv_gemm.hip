@@ -2,11 +2,16 @@
 // ("Feat/mps gemm 4bit bf16", table "What runs natively now": gemm_4bit).
 //
 // The pages' design dequantizes into a scratch buffer and then runs a GEMM.
-// Here the weight never leaves the chip in bf16: each 128 x 64 weight tile is
-// read packed (32 bytes per row), dequantized by VALU into an LDS tile, and
-// consumed by bf16 matrix-core instructions (v_mfma_f32_32x32x16_bf16) with
-// fp32 accumulation.  A 256-thread workgroup computes a 128 x 128 C tile as
-// 2 x 2 waves of 64 x 64.
+// Here the weight never leaves the chip in bf16: it is read packed, decoded
+// on the fly and consumed by bf16 matrix-core instructions
+// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.  Three kernels, by the
+// number of rows M (launch_gemm_4bit picks one):
+//  * gemm_4bit_narrow_kernel (M <= 16): split-K over 32-column workgroups,
+//    operands staged through LDS-direct loads, block scale applied per step;
+//  * gemm_4bit_skinny_kernel (M <= 64): split-K over 32-column workgroups,
+//    operands loaded straight into registers;
+//  * gemm_4bit_kernel (the rest): BM x BN C tiles, weight tiles dequantized
+//    by VALU into double-buffered LDS tiles.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
 }
 
 // ---------------------------------------------------------------------------
-// Skinny M (M <= 32 MT): gemm_4bit_skinny_kernel
+// Skinny M (M <= 32 MT <= 64): gemm_4bit_skinny_kernel
 //
 // A workgroup of KW waves owns 32 output columns (weight rows n0 .. n0 + 31)
 // and all M rows (MT tiles of 32); its waves split K (wave w takes the 64-wide
