@@ -152,6 +152,23 @@ int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_
                   const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
                   qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, void *stream);
 
+/*
+ * gemm_4bit_backward: the input gradient of a 4-bit linear layer ("Feat/mps
+ * gemm 4bit bf16", table "What runs natively now": gemm_4bit_backward, the
+ * fused form of grad_output @ dequantize_4bit(B)).
+ *   dX[m, k] = sum_n dY[m, n] * W_hat[n, k], fp32 accumulation.
+ *   dY [M, N] device row-major bf16;  dX [M, K] device row-major, dx_dtype
+ *   W_hat [N, K] as for gemm_4bit (the same packed codes and scales).
+ * The weight is dequantized tile by tile into LDS exactly as by
+ * dequantize_4bit to bf16 and multiplied with bf16 matrix cores.
+ * Requires dy_dtype == QMV_BF16, N % 32 == 0, K % blocksize == 0 and
+ * K % 32 == 0, else QMV_ERR_UNSUPPORTED.  Buffers are the caller's; dX is
+ * fully overwritten.
+ */
+int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_t N, int64_t K,
+                           const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
+                           qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *stream);
+
 /* Host-side: the 16 fp32 code values the kernels use, by code. */
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]);
 

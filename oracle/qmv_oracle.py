@@ -1,5 +1,6 @@
 """Plain CPU oracle: 4-bit blockwise quantization (NF4 / FP4), double-quantized
-absmax, dequantization and the dequantize-then-multiply (gemv / gemm).
+absmax, dequantization and the dequantize-then-multiply (gemv / gemm and the
+gemm input gradient).
 
 TEST INFRASTRUCTURE ONLY.  This module exists to check the GPU library.  Only
 ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -73,6 +74,7 @@ __all__ = [
     "nearest_codes_threshold", "pack_nibbles", "unpack_nibbles",
     "quantize_4bit", "mean_fixed_tree", "double_quant", "dequant_absmax",
     "dequantize_4bit", "dequantize_rows", "matmul_4bit", "matmul_4bit_rows",
+    "matmul_4bit_backward",
 ]
 
 NF4_DELTA = 0.9677083      # R1
@@ -356,6 +358,15 @@ def matmul_4bit(X, packed, absmax_hat, N: int, K: int, blocksize: int,
     the definition they are checked against."""
     W = dequantize_4bit(packed, absmax_hat, N * K, blocksize, quant_type).reshape(N, K)
     return np.asarray(X, dtype=np.float64).reshape(-1, K) @ W.astype(np.float64).T
+
+
+def matmul_4bit_backward(dY, packed, absmax_hat, N: int, K: int, blocksize: int,
+                         quant_type: str = "nf4") -> np.ndarray:
+    """dX[M, K] = dY[M, N] @ W_hat[N, K] in float64.  "What runs natively
+    now" (gemm_4bit_backward) and the paragraph after it: the op's default is
+    grad_output @ dequantize_4bit(B), which is therefore its definition."""
+    W = dequantize_4bit(packed, absmax_hat, N * K, blocksize, quant_type).reshape(N, K)
+    return np.asarray(dY, dtype=np.float64).reshape(-1, N) @ W.astype(np.float64)
 
 
 def matmul_4bit_rows(X, packed, absmax_hat, N: int, K: int, blocksize: int,

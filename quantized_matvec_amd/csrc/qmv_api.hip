@@ -234,6 +234,24 @@ int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_
                                         quant_type, C, c_dtype, (hipStream_t)stream));
 }
 
+int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_t N, int64_t K,
+                           const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
+                           qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *stream) {
+  if (!dY || !packed || !dX || !valid_dtype(dy_dtype) || !valid_dtype(dx_dtype))
+    return QMV_ERR_INVALID_ARG;
+  int rc = check_matmul(M, N, K, blocksize, quant_type);
+  if (rc != QMV_OK) return rc;
+  if (dy_dtype != QMV_BF16 || N % 32 != 0) return QMV_ERR_UNSUPPORTED;
+  if ((M + 127) / 128 > 65535) return QMV_ERR_UNSUPPORTED;
+  Scales sc;
+  bool dq;
+  rc = check_scales(scales, &sc, &dq);
+  if (rc != QMV_OK) return rc;
+  if (!aligned16(dY) || !aligned16(packed) || !aligned16(dX)) return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_gemm_4bit_backward(dY, M, N, K, packed, sc, dq, log2_exact(blocksize),
+                                                 quant_type, dX, dx_dtype, (hipStream_t)stream));
+}
+
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]) {
   if (!out16 || !valid_qt(quant_type)) return QMV_ERR_INVALID_ARG;
   const uint32_t *bits = table_bits(quant_type);

@@ -657,4 +657,213 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// gemm_4bit_backward: dX[M, K] = dY[M, N] @ W_hat[N, K] ("Feat/mps gemm 4bit
+// bf16", table "What runs natively now": gemm_4bit_backward, the fused form
+// of grad_output @ dequantize_4bit(B)).
+//
+// The tile kernel's structure with the weight tile transposed on its way into
+// LDS: a workgroup computes a 128 x BN tile of dX (BN = 128 or 64 columns of
+// K) and walks the reduction over N in steps of 64.  Thread t decodes RN rows
+// (n) x 8 columns (k) of the step's weight tile -- RN 4-byte loads, 64
+// contiguous bytes per row across 16 (or 8) neighbouring threads -- and writes
+// each column's RN bf16 values as one 8- (or 4-) byte store into the LDS
+// tile kept [k][n], which is the layout the MFMA B operand reads, exactly as
+// in the forward kernel.  Dequantization is the forward's: fp32(T * a_hat)
+// rounded to bf16, so the matrix cores see the dequantize_4bit weights.
+// Requires N % 32 == 0 (a step past N is half zero) and K % 32 == 0.
+// ---------------------------------------------------------------------------
+template <int CDT, bool DQ, int BN>
+__global__ __launch_bounds__(256, 2) void gemm_4bit_dx_kernel(const uint16_t *__restrict__ dY,
+                                                              int64_t M, int64_t N, int64_t K,
+                                                              const uint8_t *__restrict__ packed,
+                                                              Scales sc, int log2bs, Table16f table,
+                                                              void *__restrict__ dXv) {
+  constexpr int BM = 128;
+  constexpr int kStage = (BM + BN) * kLd;
+  constexpr int NJ = BN / 64;     // 32-column accumulators per wave (2 x 2 waves)
+  constexpr int OCT = BN / 8;     // 8-column groups of the weight tile
+  constexpr int RN = 64 / (256 / OCT);  // weight rows per thread: 4 or 2
+  using CT = typename Storage<CDT>::type;
+  CT *dX = static_cast<CT *>(dXv);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+  __shared__ float2 lut2[256];
+  __shared__ float code2[256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int64_t k0 = (int64_t)blockIdx.x * BN;
+  const int64_t NT_ = (N + 63) / 64;  // reduction steps
+  const bool n_tail = (N % 64) != 0;  // last step has 32 of 64 rows
+
+  // loaders: dY row t / 2, 32 values of the step from 32 (t % 2); weight rows
+  // RN q .. RN q + RN - 1 of the step, columns 8 o .. 8 o + 7
+  const int lr = tid >> 1, lh = tid & 1;
+  const int o = tid % OCT, q = tid / OCT;
+  const int64_t arow = m0 + lr < M ? m0 + lr : M - 1;  // rows past M are never stored
+  const int64_t kc = k0 + 8 * o < K ? k0 + 8 * o : K - 8;  // columns past K likewise
+  uint4 ra_[2][4];
+  uint32_t rb_[2][RN];
+  float rsa_[2][RN];
+  uint32_t rsq_[2][RN];
+  auto load_step = [&](int64_t st, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+    int64_t n = st * 64 + 32 * lh;
+    if (n >= N) n = N - 32;  // the missing half of a tail step (zeroed when staged)
+    const uint4 *ap = reinterpret_cast<const uint4 *>(dY + arow * N + n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra_[SL][i] = ap[i];
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+      int64_t row = st * 64 + RN * q + r;
+      if (row >= N) row = N - 1;  // zeroed when staged
+      const int64_t e0 = row * K + kc;
+      rb_[SL][r] = *reinterpret_cast<const uint32_t *>(packed + (e0 >> 1));
+      const int64_t b = e0 >> log2bs;
+      if constexpr (DQ) {
+        rsq_[SL][r] = sc.q[b];
+        rsa_[SL][r] = sc.absmax2[b >> sc.log2bs2];
+      } else {
+        rsa_[SL][r] = sc.absmax[b];
+      }
+    }
+  };
+  auto stage_step = [&](int64_t st, int buf, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+    uint16_t *As = smem + buf * kStage;
+    uint16_t *Bs = As + BM * kLd;
+    const bool last = n_tail && st == NT_ - 1;
+    uint4 *ad = reinterpret_cast<uint4 *>(As + lr * kLd + 32 * lh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = (last && lh == 1) ? make_uint4(0, 0, 0, 0) : ra_[SL][i];
+    // w[r][i]: bf16 pair (column 8 o + 2 i, 8 o + 2 i + 1) of weight row r
+    uint32_t w[RN][4];
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+      const bool zero = last && RN * q + r >= 32;
+      const float a = zero ? 0.f : (DQ ? code2[rsq_[SL][r]] * rsa_[SL][r] + sc_offset(sc) : rsa_[SL][r]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 t = lut2[(rb_[SL][r] >> (8 * i)) & 0xffu];
+        const f32x2_t v = {materialize(t.x * a), materialize(t.y * a)};
+        w[r][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+      }
+    }
+    // column c = 8 o + 2 i (+1): its RN values, rows in order, in one store
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const uint32_t sel = hi ? 0x07060302u : 0x05040100u;  // high or low bf16 of each pair
+        uint16_t *dst = Bs + (8 * o + 2 * i + hi) * kLd + RN * q;
+        if constexpr (RN == 4) {
+          const uint32_t x0 = __builtin_amdgcn_perm(w[1][i], w[0][i], sel);
+          const uint32_t x1 = __builtin_amdgcn_perm(w[3][i], w[2][i], sel);
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(x0, x1);
+        } else {
+          *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(w[1][i], w[0][i], sel);
+        }
+      }
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load_step(0, S0{});
+  load_step(NT_ > 1 ? 1 : 0, S1{});
+  lut2[tid] = make_float2(table.v[tid >> 4], table.v[tid & 15]);
+  if constexpr (DQ) code2[tid] = sc.code2[tid];
+  __syncthreads();
+  stage_step(0, 0, S0{});
+  __syncthreads();
+
+  f32x16_t acc[2][NJ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mma_step = [&](int buf) {
+    const uint16_t *As = smem + buf * kStage;
+    const uint16_t *Bs = As + BM * kLd;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t af[2], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8_t *>(As + row * kLd + ks * 16 + (lane >> 5) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = wn * (BN / 2) + j * 32 + (lane & 31);
+        bfr[j] = *reinterpret_cast<const bf16x8_t *>(Bs + col * kLd + ks * 16 + (lane >> 5) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // step st sits in LDS stage st % 2 and step st + 1 in register set (st + 1) % 2;
+  // loads past the end re-read the last step, so they are unconditional
+  auto clampn = [&](int64_t st) { return st < NT_ ? st : NT_ - 1; };
+  int64_t st = 0;
+  for (; st + 1 < NT_; st += 2) {
+    load_step(clampn(st + 2), S0{});
+    mma_step(0);
+    stage_step(st + 1, 1, S1{});
+    __syncthreads();
+    load_step(clampn(st + 3), S1{});
+    mma_step(1);
+    if (st + 2 < NT_) stage_step(st + 2, 0, S0{});
+    __syncthreads();
+  }
+  if (st < NT_) mma_step(0);
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = k0 + wn * (BN / 2) + j * 32 + (lane & 31);
+      if (col >= K) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) store_elem<CDT>(dX, row * K + col, acc[i][j][r]);
+      }
+    }
+}
+
+hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                     int qt, void *dX, int dx_dtype, hipStream_t st) {
+  const uint16_t *g = static_cast<const uint16_t *>(dY);
+  Table16f table;
+  const uint32_t *bits = table_bits(qt);
+  for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
+  const int64_t mt = (M + 127) / 128;
+  const bool wide = ((K + 127) / 128) * mt >= (int64_t)device_cu_count();
+  const dim3 grid((unsigned)(wide ? (K + 127) / 128 : (K + 63) / 64), (unsigned)mt);
+#define QMV_B(CDT, DQV, BNV)                                                                        \
+  hipLaunchKernelGGL((gemm_4bit_dx_kernel<CDT, DQV, BNV>), grid, dim3(256), 0, st, g, M, N, K, packed, \
+                     sc, log2bs, table, dX)
+#define QMV_BB(CDT, DQV) \
+  if (wide) { QMV_B(CDT, DQV, 128); } else { QMV_B(CDT, DQV, 64); }
+#define QMV_BD(CDT) \
+  if (dq) { QMV_BB(CDT, true); } else { QMV_BB(CDT, false); }
+  if (dx_dtype == kF32) { QMV_BD(kF32); }
+  else if (dx_dtype == kF16) { QMV_BD(kF16); }
+  else { QMV_BD(kBF16); }
+#undef QMV_BD
+#undef QMV_BB
+#undef QMV_B
+  return hipGetLastError();
+}
+
 }  // namespace qmv

@@ -57,4 +57,8 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
                             const Scales &sc, bool dq, int log2bs, int qt, void *C, int c_dtype,
                             hipStream_t st);
 
+hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                     int qt, void *dX, int dx_dtype, hipStream_t st);
+
 }  // namespace qmv

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_gemm_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
                                          ctypes.c_int, vp, ctypes.c_int, vp]),
+        "qmv_gemm_4bit_backward": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
+                                                  ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
         "qmv_default_code2": (ctypes.c_int, [vp]),
         "qmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -237,6 +239,29 @@ def gemm_4bit(A: torch.Tensor, packed: torch.Tensor, state: QuantState,
               out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None):
     """C [M, N] = A [M, K] @ W_hat^T (A in bf16)."""
     return _matmul("gemm_4bit", A, packed, state, out, out_dtype)
+
+
+def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState,
+                       out: Optional[torch.Tensor] = None,
+                       out_dtype: Optional[torch.dtype] = None):
+    """dX [M, K] = dY [M, N] @ W_hat (dY in bf16): the input gradient of y = x @ W_hat^T."""
+    if len(state.shape) != 2:
+        raise ValueError("the quantized weight must be 2-D [N, K]")
+    N, K = state.shape
+    packed = _dev(packed, "packed")
+    dY = _dev(dY, "dY")
+    g2 = dY.reshape(-1, N)
+    M = g2.shape[0]
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype or dY.dtype, device=dY.device)
+    elif not out.is_contiguous() or out.numel() != M * K or out.data_ptr() % 16:
+        raise ValueError("out must be contiguous, 16-byte aligned and hold M * K elements")
+    c = state._c()
+    _check(lib().qmv_gemm_4bit_backward(g2.data_ptr(), _DT[g2.dtype], M, N, K, packed.data_ptr(),
+                                        ctypes.byref(c), state.blocksize, _QT[state.quant_type],
+                                        out.data_ptr(), _DT[out.dtype], _stream(g2)),
+           "gemm_4bit_backward")
+    return out
 
 
 def code_table(quant_type: str = "nf4") -> list:

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(qmvlib, n), n
 
@@ -129,6 +129,13 @@ def test_matmul_preconditions(qmvlib):
     assert gm(P, BF16, 8, 64, 64, P, r, 100, NF4, P, BF16, None) == UNSUPPORTED
     assert gm(P, BF16, 8, 64, 64, P, None, 64, NF4, P, BF16, None) == INVALID
     assert gm(P, BF16, 8, 64, 64, P, r, 64, 2, P, BF16, None) == INVALID
+    gb = qmvlib.qmv_gemm_4bit_backward  # dY [M, N] @ W_hat [N, K]
+    assert gb(P, F16, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED    # dY must be bf16
+    assert gb(P, BF16, 8, 48, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # N % 32
+    assert gb(P, BF16, 8, 64, 96, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # K % bs
+    assert gb(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
+    assert gb(None, BF16, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
+    assert gb(P, BF16, 8, 64, 64, P, r, 64, NF4, MIS, BF16, None) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors(qmvlib):

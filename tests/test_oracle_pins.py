@@ -381,6 +381,29 @@ def test_gemm_bruteforce_fsum_small():
         rtol=1e-13, atol=1e-16)
 
 
+def test_backward_is_the_adjoint_of_the_forward():
+    """<dY, X W^T> = <dY W, X> for any X and dY (the backward of y = x W^T
+    with respect to x), and a one-hot dY row returns that weight row exactly:
+    a transposed or mis-indexed weight fails one of the two."""
+    N, K, bs = 24, 128, 32
+    _, packed, absmax = _small_state(N, K, bs, "nf4", seed=9)
+    rng = np.random.default_rng(10)
+    X = rng.standard_normal((5, K))
+    dY = rng.standard_normal((5, N))
+    Y = O.matmul_4bit(X, packed, absmax, N, K, bs)
+    dX = O.matmul_4bit_backward(dY, packed, absmax, N, K, bs)
+    assert dX.shape == (5, K)
+    lhs = math.fsum((dY * Y).ravel())
+    rhs = math.fsum((dX * X).ravel())
+    assert lhs == pytest.approx(rhs, rel=1e-12, abs=1e-14)
+    What = O.dequantize_4bit(packed, absmax, N * K, bs).reshape(N, K)
+    for n in (0, 7, 23):
+        e = np.zeros((1, N))
+        e[0, n] = 1.0
+        assert np.array_equal(O.matmul_4bit_backward(e, packed, absmax, N, K, bs)[0],
+                              What[n].astype(np.float64))
+
+
 def test_quantize_full_pipeline_small_bf16_roundtrip():
     """dequant(quant(x)) stays within the code gaps for DQ'd scales too."""
     rng = np.random.default_rng(8)
