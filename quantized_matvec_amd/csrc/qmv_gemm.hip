@@ -673,41 +673,49 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
 // rounded to bf16, so the matrix cores see the dequantize_4bit weights.
 // Requires N % 32 == 0 (a step past N is half zero) and K % 32 == 0.
 // ---------------------------------------------------------------------------
-template <int CDT, bool DQ, int BN>
-__global__ __launch_bounds__(256, 2) void gemm_4bit_dx_kernel(const uint16_t *__restrict__ dY,
-                                                              int64_t M, int64_t N, int64_t K,
-                                                              const uint8_t *__restrict__ packed,
-                                                              Scales sc, int log2bs, Table16f table,
-                                                              void *__restrict__ dXv) {
+template <int CDT, bool DQ, int BN, int G>
+__global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint16_t *__restrict__ dY,
+                                                                      int64_t M, int64_t N, int64_t K,
+                                                                      const uint8_t *__restrict__ packed,
+                                                                      Scales sc, int log2bs, Table16f table,
+                                                                      void *__restrict__ dXv) {
   constexpr int BM = 128;
   constexpr int kStage = (BM + BN) * kLd;
-  constexpr int NJ = BN / 64;     // 32-column accumulators per wave (2 x 2 waves)
+  constexpr int NJ = BN / 64;     // 32-column accumulators per wave (2 x 2 waves per group)
   constexpr int OCT = BN / 8;     // 8-column groups of the weight tile
   constexpr int RN = 64 / (256 / OCT);  // weight rows per thread: 4 or 2
   using CT = typename Storage<CDT>::type;
   CT *dX = static_cast<CT *>(dXv);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_all[G * 2 * kStage];
   __shared__ float2 lut2[256];
   __shared__ float code2[256];
   const int tid = threadIdx.x;
+  const int grp = tid >> 8;       // group: takes reduction steps grp, grp + G, ...
+  const int t = tid & 255;        // thread within the group
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = t >> 6;        // wave within the group
   const int wm = wave >> 1, wn = wave & 1;
+  uint16_t *smem = smem_all + grp * 2 * kStage;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t k0 = (int64_t)blockIdx.x * BN;
   const int64_t NT_ = (N + 63) / 64;  // reduction steps
+  const int64_t NL = (NT_ + G - 1) / G;  // steps per group (the last may be past the end)
   const bool n_tail = (N % 64) != 0;  // last step has 32 of 64 rows
 
   // loaders: dY row t / 2, 32 values of the step from 32 (t % 2); weight rows
   // RN q .. RN q + RN - 1 of the step, columns 8 o .. 8 o + 7
-  const int lr = tid >> 1, lh = tid & 1;
-  const int o = tid % OCT, q = tid / OCT;
+  const int lr = t >> 1, lh = t & 1;
+  const int o = t % OCT, q = t / OCT;
   const int64_t arow = m0 + lr < M ? m0 + lr : M - 1;  // rows past M are never stored
   const int64_t kc = k0 + 8 * o < K ? k0 + 8 * o : K - 8;  // columns past K likewise
   uint4 ra_[2][4];
   uint32_t rb_[2][RN];
   float rsa_[2][RN];
   uint32_t rsq_[2][RN];
+  auto gstep = [&](int64_t l) {  // the group's l-th step, clamped to the last one
+    const int64_t s2 = grp + (int64_t)G * l;
+    return s2 < NT_ ? s2 : NT_ - 1;
+  };
   auto load_step = [&](int64_t st, auto slot_tag) {
     constexpr int SL = decltype(slot_tag)::value;
     int64_t n = st * 64 + 32 * lh;
@@ -746,8 +754,8 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_dx_kernel(const uint16_t *__
       const float a = zero ? 0.f : (DQ ? code2[rsq_[SL][r]] * rsa_[SL][r] + sc_offset(sc) : rsa_[SL][r]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float2 t = lut2[(rb_[SL][r] >> (8 * i)) & 0xffu];
-        const f32x2_t v = {materialize(t.x * a), materialize(t.y * a)};
+        const float2 tv = lut2[(rb_[SL][r] >> (8 * i)) & 0xffu];
+        const f32x2_t v = {materialize(tv.x * a), materialize(tv.y * a)};
         w[r][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
       }
     }
@@ -771,12 +779,14 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_dx_kernel(const uint16_t *__
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  load_step(0, S0{});
-  load_step(NT_ > 1 ? 1 : 0, S1{});
-  lut2[tid] = make_float2(table.v[tid >> 4], table.v[tid & 15]);
-  if constexpr (DQ) code2[tid] = sc.code2[tid];
+  load_step(gstep(0), S0{});
+  load_step(gstep(1), S1{});
+  if (tid < 256) {
+    lut2[tid] = make_float2(table.v[tid >> 4], table.v[tid & 15]);
+    if constexpr (DQ) code2[tid] = sc.code2[tid];
+  }
   __syncthreads();
-  stage_step(0, 0, S0{});
+  stage_step(gstep(0), 0, S0{});
   __syncthreads();
 
   f32x16_t acc[2][NJ];
@@ -786,7 +796,8 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_dx_kernel(const uint16_t *__
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto mma_step = [&](int buf) {
+  auto mma_step = [&](int64_t l, int buf) {
+    if (grp + (int64_t)G * l >= NT_) return;  // past this group's last step (wave-uniform)
     const uint16_t *As = smem + buf * kStage;
     const uint16_t *Bs = As + BM * kLd;
 #pragma unroll
@@ -810,21 +821,47 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_dx_kernel(const uint16_t *__
     }
   };
 
-  // step st sits in LDS stage st % 2 and step st + 1 in register set (st + 1) % 2;
-  // loads past the end re-read the last step, so they are unconditional
-  auto clampn = [&](int64_t st) { return st < NT_ ? st : NT_ - 1; };
-  int64_t st = 0;
-  for (; st + 1 < NT_; st += 2) {
-    load_step(clampn(st + 2), S0{});
-    mma_step(0);
-    stage_step(st + 1, 1, S1{});
+  // the group's step l sits in LDS stage l % 2 and step l + 1 in register set
+  // (l + 1) % 2; loads past the end re-read the last step, so every group
+  // runs the same loop (and the same barriers)
+  int64_t l = 0;
+  for (; l + 1 < NL; l += 2) {
+    load_step(gstep(l + 2), S0{});
+    mma_step(l, 0);
+    stage_step(gstep(l + 1), 1, S1{});
     __syncthreads();
-    load_step(clampn(st + 3), S1{});
-    mma_step(1);
-    if (st + 2 < NT_) stage_step(st + 2, 0, S0{});
+    load_step(gstep(l + 3), S1{});
+    mma_step(l + 1, 1);
+    if (l + 2 < NL) stage_step(gstep(l + 2), 0, S0{});
     __syncthreads();
   }
-  if (st < NT_) mma_step(0);
+  if (l < NL) mma_step(l, 0);
+
+  if constexpr (G > 1) {  // add the other groups' tiles, in group order
+    float *part = reinterpret_cast<float *>(smem_all);
+    constexpr int PER = 2 * NJ * 16;  // floats per lane
+    __syncthreads();
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            part[(((grp - 1) * 4 + wave) * PER + (i * NJ + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g2 = 1; g2 < G; ++g2)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] += part[(((g2 - 1) * 4 + wave) * PER + (i * NJ + j) * 16 + r) * 64 + lane];
+  }
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -850,9 +887,9 @@ hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64
   const int64_t mt = (M + 127) / 128;
   const bool wide = ((K + 127) / 128) * mt >= (int64_t)device_cu_count();
   const dim3 grid((unsigned)(wide ? (K + 127) / 128 : (K + 63) / 64), (unsigned)mt);
-#define QMV_B(CDT, DQV, BNV)                                                                        \
-  hipLaunchKernelGGL((gemm_4bit_dx_kernel<CDT, DQV, BNV>), grid, dim3(256), 0, st, g, M, N, K, packed, \
-                     sc, log2bs, table, dX)
+#define QMV_B(CDT, DQV, BNV)                                                                    \
+  hipLaunchKernelGGL((gemm_4bit_dx_kernel<CDT, DQV, BNV, 2>), grid, dim3(512), 0, st, g, M, N, K, \
+                     packed, sc, log2bs, table, dX)
 #define QMV_BB(CDT, DQV) \
   if (wide) { QMV_B(CDT, DQV, 128); } else { QMV_B(CDT, DQV, 64); }
 #define QMV_BD(CDT) \
