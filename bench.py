@@ -11,6 +11,8 @@ gemm_4bit (M = 512).  The headline value is gemv_4bit's achieved HBM
 bandwidth: algorithmic bytes per launch / average launch duration, timed with
 HIP events on the launch stream while rotating over distinct weight copies
 (> 512 MB, twice the 256 MB Infinity Cache) so the bytes come from HBM.
+Each kernel is also timed alone, including gemm_4bit_backward (dX = dY @
+W_hat with a bf16 dY [512, 14336]), which is not part of the step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -257,7 +259,17 @@ def main():
             L.qmv_double_quant(abuf[i % n_w].data_ptr(), nbk, BS2, None, q.data_ptr(), a2.data_ptr(),
                                off.data_ptr(), c2.data_ptr(), ws.data_ptr(), ws.numel(), s_h)
 
+        # gemm_4bit_backward (dX = dY @ W_hat) on the same weight, dY [512, 14336]
+        dY = synth.gaussian((M_GEMM, N), 1.0, 100 * 4 + 3, "bf16").to(dev)
+        dX = torch.empty(M_GEMM, K, dtype=torch.bfloat16, device=dev)
+        dY_ptr, dX_ptr = dY.data_ptr(), dX.data_ptr()
+
+        def run_bwd(i):
+            L.qmv_gemm_4bit_backward(dY_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0,
+                                     dX_ptr, 2, s_h)
+
         for name, fn, iters in (("gemv_4bit", run_gemv, kiters), ("gemm_4bit", run_gemm, kiters // 4),
+                                ("gemm_4bit_backward", run_bwd, kiters // 8),
                                 ("dequantize_4bit", run_deq, kiters // 4),
                                 ("quantize_4bit", run_quant, kiters // 4),
                                 ("double_quant", run_dq, kiters // 4)):
@@ -271,7 +283,7 @@ def main():
         if name == "gemv_4bit" or name == "dequantize_4bit":
             b = ab[name]
             e.update(bytes=b, gbs=round(b / us / 1e3, 1), hbm_frac=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
-        elif name == "gemm_4bit":
+        elif name in ("gemm_4bit", "gemm_4bit_backward"):
             fl = 2.0 * M_GEMM * N * K
             e.update(flops=fl, tflops=round(fl / us / 1e6, 2),
                      mfma_frac=round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4))
