@@ -153,6 +153,30 @@ int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_
                   qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, void *stream);
 
 /*
+ * quantize_blockwise / dequantize_blockwise: the general 8-bit blockwise codec
+ * ("Feat/mps gemm 4bit bf16", table "What runs natively now": quantize_blockwise
+ * / dequantize_blockwise; "Known failures": the exact float64 nearest-code
+ * search is the reference, a normalised-value lookup table is not).
+ *   quantize:   absmax[b] = max |A_i| over block b (fp32, exact);
+ *               q[i] = code index nearest to A_i / absmax[b], exactly (ties
+ *               toward zero; a zero block gives the code of 0, whose index
+ *               is the table's).
+ *   dequantize: out[i] = fp32(code[q[i]] * absmax[i / blocksize]), rounded to
+ *               out_dtype (round to nearest even).
+ *   A          [n] device, a_dtype (fp32 / fp16 / bf16)
+ *   q          [n] device uint8;  absmax [ceil(n / blocksize)] device fp32
+ *   blocksize  power of two in [32, 4096]
+ *   code_host  [256] HOST fp32 table (as for qmv_double_quant: strictly
+ *              increasing, midpoints exact with <= 29 significant bits, else
+ *              QMV_ERR_UNSUPPORTED), or NULL for (k - 127) / 127.
+ * Buffers are the caller's, 16-byte aligned (QMV_ERR_ALIGNMENT).
+ */
+int qmv_quantize_blockwise(const void *A, qmv_dtype a_dtype, int64_t n, int32_t blocksize,
+                           const float *code_host, uint8_t *q, float *absmax, void *stream);
+int qmv_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, int32_t blocksize,
+                             const float *code_host, void *out, qmv_dtype out_dtype, void *stream);
+
+/*
  * gemm_4bit_backward: the input gradient of a 4-bit linear layer ("Feat/mps
  * gemm 4bit bf16", table "What runs natively now": gemm_4bit_backward, the
  * fused form of grad_output @ dequantize_4bit(B)).

@@ -74,7 +74,8 @@ __all__ = [
     "nearest_codes_threshold", "pack_nibbles", "unpack_nibbles",
     "quantize_4bit", "mean_fixed_tree", "double_quant", "dequant_absmax",
     "dequantize_4bit", "dequantize_rows", "matmul_4bit", "matmul_4bit_rows",
-    "matmul_4bit_backward",
+    "matmul_4bit_backward", "dynamic_tree_table", "quantize_blockwise",
+    "dequantize_blockwise",
 ]
 
 NF4_DELTA = 0.9677083      # R1
@@ -309,6 +310,50 @@ def dequant_absmax(q, absmax2, offset, code2=None, blocksize2: int = 256) -> np.
     s = np.repeat(np.asarray(absmax2, dtype=np.float32), blocksize2)[: q.size]
     prod = code2[q] * s                                   # fp32 multiply, RN
     return (prod + np.float32(offset)).astype(np.float32) # fp32 add, RN
+
+
+# --------------------------------------------------------------------------
+# 8-bit blockwise codec (R10, R11)
+# --------------------------------------------------------------------------
+def dynamic_tree_table() -> np.ndarray:
+    """R11: the signed dynamic-tree 8-bit table.  After the sign, a run of e
+    zero bits (e = 0..6) selects the decimal exponent and the bits after the
+    first one bit (6 - e of them) a linear fraction: the centre of bin j of
+    [0.1, 1] cut into 2^(6-e) equal bins.  Values 10^-e * centre, their
+    negatives, 0 and 1, rounded once to fp32 and sorted (256 values)."""
+    mags = []
+    for e in range(7):
+        bins = 2 ** (6 - e)
+        width = 0.9 / bins
+        for j in range(bins):
+            centre = 0.1 + width * (j + 0.5)
+            mags.append(np.float32(centre * 10.0 ** (-e)))
+    vals = [np.float32(0.0), np.float32(1.0)] + mags + [np.float32(-m) for m in mags]
+    t = np.array(sorted(set(float(v) for v in vals)), dtype=np.float32)
+    assert t.size == 256
+    return t
+
+
+def quantize_blockwise(x, blocksize: int, code=None):
+    """R10: 8-bit blockwise codec.  "What runs natively now": quantize_blockwise
+    (8-bit); "Known failures": the reference is an exact float64 nearest-code
+    search.  absmax[b] = max |x| over block b (fp32, exact); q = exact nearest
+    code of x / absmax[b] (R3's tie rule; a zero block takes the code of 0).
+    Returns (q uint8 [n], absmax fp32 [ceil(n / blocksize)])."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    code = linear8_table() if code is None else np.asarray(code, dtype=np.float32)
+    a = block_absmax(x, blocksize)
+    a_el = np.repeat(a, blocksize)[: x.size]
+    q = nearest_codes(x, a_el, code)
+    return q.astype(np.uint8), a.astype(np.float32)
+
+
+def dequantize_blockwise(q, absmax, blocksize: int, code=None, out_dtype: str = "fp32"):
+    """R10: w = fp32(code[q] * absmax[block]), then rounded to the output type."""
+    q = np.asarray(q, dtype=np.int64).ravel()
+    code = linear8_table() if code is None else np.asarray(code, dtype=np.float32)
+    a = np.repeat(np.asarray(absmax, dtype=np.float32), blocksize)[: q.size]
+    return _cast_out((code[q] * a).astype(np.float32), out_dtype)
 
 
 # --------------------------------------------------------------------------

@@ -142,6 +142,23 @@ static int check_code2(const Code2Table &t) {
   return QMV_OK;
 }
 
+// The caller's table (or the default), validated as for double_quant.
+static int code_table8(const float *code_host, Code2Table &t, bool &linear) {
+  static const Code2Table kDefault = [] {
+    Code2Table d{};
+    qmv_default_code2(d.v);
+    return d;
+  }();
+  static const int kDefaultStatus = check_code2(kDefault);
+  t = kDefault;
+  linear = true;
+  if (code_host) {
+    memcpy(t.v, code_host, sizeof(t.v));
+    linear = memcmp(t.v, kDefault.v, sizeof(t.v)) == 0;
+  }
+  return linear ? kDefaultStatus : check_code2(t);
+}
+
 int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
                      const float *code2_host, uint8_t *absmax_q, float *absmax2, float *offset,
                      float *code2_out, void *workspace, size_t workspace_bytes, void *stream) {
@@ -154,23 +171,39 @@ int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
       !aligned16(code2_out) || !aligned16(workspace))
     return QMV_ERR_ALIGNMENT;
   // the default table is checked once; a caller's table on every call
-  static const Code2Table kDefault = [] {
-    Code2Table d{};
-    qmv_default_code2(d.v);
-    return d;
-  }();
-  static const int kDefaultStatus = check_code2(kDefault);
-  Code2Table t = kDefault;
-  bool linear = true;
-  if (code2_host) {
-    memcpy(t.v, code2_host, sizeof(t.v));
-    linear = memcmp(t.v, kDefault.v, sizeof(t.v)) == 0;
-  }
-  const int rc = linear ? kDefaultStatus : check_code2(t);
+  Code2Table t;
+  bool linear;
+  const int rc = code_table8(code2_host, t, linear);
   if (rc != QMV_OK) return rc;
   return launch_status(launch_double_quant(absmax, nblocks, log2_exact(blocksize2), t, linear,
                                            absmax_q, absmax2, offset, code2_out, workspace,
                                            (hipStream_t)stream));
+}
+
+int qmv_quantize_blockwise(const void *A, qmv_dtype a_dtype, int64_t n, int32_t blocksize,
+                           const float *code_host, uint8_t *q, float *absmax, void *stream) {
+  if (!A || !q || !absmax || n <= 0 || !valid_dtype(a_dtype)) return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize)) return QMV_ERR_UNSUPPORTED;
+  if (!aligned16(A) || !aligned16(q) || !aligned16(absmax)) return QMV_ERR_ALIGNMENT;
+  Code2Table t;
+  bool linear;
+  const int rc = code_table8(code_host, t, linear);
+  if (rc != QMV_OK) return rc;
+  return launch_status(launch_quantize_blockwise(A, a_dtype, n, log2_exact(blocksize), t, linear, q,
+                                                 absmax, (hipStream_t)stream));
+}
+
+int qmv_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, int32_t blocksize,
+                             const float *code_host, void *out, qmv_dtype out_dtype, void *stream) {
+  if (!q || !absmax || !out || n <= 0 || !valid_dtype(out_dtype)) return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize)) return QMV_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(absmax) || !aligned16(out)) return QMV_ERR_ALIGNMENT;
+  Code2Table t;
+  bool linear;
+  const int rc = code_table8(code_host, t, linear);
+  if (rc != QMV_OK) return rc;
+  return launch_status(launch_dequantize_blockwise(q, absmax, n, log2_exact(blocksize), t, out,
+                                                   out_dtype, (hipStream_t)stream));
 }
 
 int qmv_dequantize_absmax(const qmv_absmax *scales, int64_t nblocks, float *absmax_out,

@@ -18,7 +18,6 @@
 
 namespace qmv {
 
-static int device_cus();
 
 int log2_exact(int64_t v) {
   int l = 0;
@@ -317,7 +316,7 @@ static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, co
   constexpr int E = 16;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, 8 * device_cus()));
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, 8 * device_cu_count()));
   hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, E>), dim3(grid), dim3(256), 0, st, W, numel,
                      log2bs, qa, packed, absmax);
   return hipGetLastError();
@@ -649,8 +648,12 @@ __device__ __forceinline__ float fused_offset(const double *__restrict__ levels,
   return (float)__ddiv_rn(total, (double)n);
 }
 
-template <int E>
-__global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict__ absmax,
+//
+// The same kernel is the 8-bit blockwise codec (quantize_blockwise): DT is the
+// input type (fp32 for the scales) and ZOFF drops the offset (c = x), so the
+// group max is the block absmax and q the nearest code of x / absmax.
+template <int E, int DT, bool ZOFF>
+__global__ __launch_bounds__(256) void dq_encode_kernel(const void *__restrict__ absmax_v,
                                                         int64_t n, int log2bs2, Code2Table code2,
                                                         int linear, const double *__restrict__ levels,
                                                         const int2 *__restrict__ stats, int64_t nl,
@@ -658,6 +661,8 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ absmax2,
                                                         float *__restrict__ code2_out) {
+  using T = typename Storage<DT>::type;
+  const T *absmax = static_cast<const T *>(absmax_v);
   __shared__ double mid[256];
   __shared__ float wave_max[4];
   __shared__ double red[kTopFused / kFanIn];
@@ -665,9 +670,11 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (tid < 255) mid[tid] = ((double)code2.v[tid] + (double)code2.v[tid + 1]) * 0.5;  // exact
-  if (blockIdx.x == 0) code2_out[tid] = code2.v[tid];
+  if (code2_out && blockIdx.x == 0) code2_out[tid] = code2.v[tid];
   float off;
-  if (nl > 1 && nl <= kTopFused) {
+  if (ZOFF) {
+    off = 0.f;
+  } else if (nl > 1 && nl <= kTopFused) {
     off = fused_offset(levels, nl, stats, n, red);
     if (blockIdx.x == 0 && tid == 0) offset[0] = off;
   } else {
@@ -684,12 +691,17 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
     // the tile's scales through a range-limited buffer: no branch per load
     const int64_t rem = n - t * tile;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(absmax + t * tile, (uint32_t)((rem < tile ? rem : tile) * 4));
+        make_rsrc(absmax + t * tile, (uint32_t)((rem < tile ? rem : tile) * sizeof(T)));
     float a[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rs, (uint32_t)((tid * E + e) * 4), 0, 0));
+    for (int e = 0; e < E; ++e) {
+      if constexpr (DT == kF32)
+        a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rs, (uint32_t)((tid * E + e) * 4), 0, 0));
+      else
+        a[e] = bits16_to_f32<DT>((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+            rs, (uint32_t)((tid * E + e) * 2), 0, 0));
+    }
     float c[E];
     float m = 0.f;
 #pragma unroll
@@ -719,10 +731,14 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
     };
     int code[E];
     if (linear) {
-      const float inv = m > 0.f ? 127.f / m : 0.f;
+      // first guess k ~ 127 c / m in fp32 (the exact thresholds below fix it
+      // by one step); a block with a tiny max is first scaled up by an exact
+      // 2^64 so that 127 / m stays finite
+      const float up = m < 0x1p-60f ? 0x1p64f : 1.f;
+      const float inv = m > 0.f ? 127.f / (m * up) : 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        int k = (int)rintf(c[e] * inv) + 127;
+        int k = (int)rintf((c[e] * up) * inv) + 127;
         k = k < 0 ? 0 : (k > 254 ? 254 : k);  // code 255 (> 1) is never nearest
         const double x = (double)c[e];
         k += (k < 255 && above(x, k)) ? 1 : 0;
@@ -789,11 +805,97 @@ hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2
   const int64_t ntiles = (nblocks + tile - 1) / tile;
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
 #define QMV_E(EV)                                                                          \
-  hipLaunchKernelGGL(dq_encode_kernel<EV>, dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
+  hipLaunchKernelGGL((dq_encode_kernel<EV, kF32, false>), dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
                      code2, linear ? 1 : 0, levels, stats, runs > kTopFused ? (int64_t)1 : runs, \
                      offset, q, absmax2, code2_out)
   if (E == 8) QMV_E(8); else QMV_E(16);
 #undef QMV_E
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit blockwise codec ("Feat/mps gemm 4bit bf16", table "What runs natively
+// now": quantize_blockwise / dequantize_blockwise; "Known failures": the
+// exact float64 nearest-code search is the reference).
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_blockwise(const void *A, int a_dtype, int64_t n, int log2bs,
+                                     const Code2Table &code, bool linear, uint8_t *q,
+                                     float *absmax, hipStream_t st) {
+  const int bs = 1 << log2bs;
+  const int E = bs > 2048 ? 16 : 8;
+  const int64_t tile = 256 * (int64_t)E;
+  const int64_t ntiles = (n + tile - 1) / tile;
+  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
+#define QMV_QB(EV, DTV)                                                                            \
+  hipLaunchKernelGGL((dq_encode_kernel<EV, DTV, true>), dim3(grid), dim3(256), 0, st, A, n, log2bs, \
+                     code, linear ? 1 : 0, nullptr, nullptr, (int64_t)1, nullptr, q, absmax, nullptr)
+#define QMV_QBD(EV)                                \
+  if (a_dtype == kF32) { QMV_QB(EV, kF32); }       \
+  else if (a_dtype == kF16) { QMV_QB(EV, kF16); }  \
+  else { QMV_QB(EV, kBF16); }
+  if (E == 8) { QMV_QBD(8); } else { QMV_QBD(16); }
+#undef QMV_QBD
+#undef QMV_QB
+  return hipGetLastError();
+}
+
+// out[i] = fp32(code[q[i]] * absmax[i / blocksize]) rounded to the output
+// type; 16 codes per thread (one 16-byte load, one block: blocks are >= 32).
+template <int ODT>
+__global__ __launch_bounds__(256) void dequantize_blockwise_kernel(const uint8_t *__restrict__ q,
+                                                                   const float *__restrict__ absmax,
+                                                                   int64_t n, int log2bs,
+                                                                   Code2Table code, void *out_v) {
+  using OT = typename Storage<ODT>::type;
+  OT *out = static_cast<OT *>(out_v);
+  __shared__ float tab[256];
+  tab[threadIdx.x] = code.v[threadIdx.x];
+  __syncthreads();
+  const int64_t chunks = (n + 15) / 16;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
+    const int64_t i0 = c * 16;
+    const float a = absmax[i0 >> log2bs];
+    if (i0 + 16 <= n) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(q + i0);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      float v[16];
+#pragma unroll
+      for (int b = 0; b < 16; ++b) v[b] = materialize(tab[(ws[b >> 2] >> (8 * (b & 3))) & 0xffu] * a);
+      if constexpr (ODT == kF32) {
+        uint4 *dst = reinterpret_cast<uint4 *>(out + i0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          dst[k] = make_uint4(__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                              __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3]));
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          h[k] = f32_to_bits16<ODT>(v[2 * k]) | (f32_to_bits16<ODT>(v[2 * k + 1]) << 16);
+        uint4 *dst = reinterpret_cast<uint4 *>(out + i0);
+        dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      }
+    } else {
+      for (int64_t i = i0; i < n; ++i) store_elem<ODT>(out, i, materialize(tab[q[i]] * a));
+    }
+  }
+}
+
+hipError_t launch_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, int log2bs,
+                                       const Code2Table &code, void *out, int out_dtype,
+                                       hipStream_t st) {
+  const int64_t chunks = (n + 15) / 16;
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, 8 * device_cu_count()));
+  if (out_dtype == kF32)
+    hipLaunchKernelGGL(dequantize_blockwise_kernel<kF32>, dim3(grid), dim3(256), 0, st, q, absmax, n,
+                       log2bs, code, out);
+  else if (out_dtype == kF16)
+    hipLaunchKernelGGL(dequantize_blockwise_kernel<kF16>, dim3(grid), dim3(256), 0, st, q, absmax, n,
+                       log2bs, code, out);
+  else
+    hipLaunchKernelGGL(dequantize_blockwise_kernel<kBF16>, dim3(grid), dim3(256), 0, st, q, absmax, n,
+                       log2bs, code, out);
   return hipGetLastError();
 }
 
@@ -945,18 +1047,6 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
   }
 }
 
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 template <int QT, int ODT>
 static hipError_t launch_dequant_t(const uint8_t *packed, const Scales &sc, bool dq, int64_t numel,
@@ -964,7 +1054,7 @@ static hipError_t launch_dequant_t(const uint8_t *packed, const Scales &sc, bool
   const int64_t nchunk = numel >> 11;
   const int64_t waves_per_wg = kDeqThreads / 64;
   const int64_t want = std::max<int64_t>(1, (nchunk + waves_per_wg * kDeqU - 1) / (waves_per_wg * kDeqU));
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 8 * device_cus()));
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 8 * device_cu_count()));
   if (dq)
     hipLaunchKernelGGL((dequantize_4bit_kernel<QT, ODT, true>), dim3(grid), dim3(kDeqThreads), 0, st,
                        packed, sc, numel, log2bs, out);

@@ -57,6 +57,14 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
                             const Scales &sc, bool dq, int log2bs, int qt, void *C, int c_dtype,
                             hipStream_t st);
 
+hipError_t launch_quantize_blockwise(const void *A, int a_dtype, int64_t n, int log2bs,
+                                     const Code2Table &code, bool linear, uint8_t *q,
+                                     float *absmax, hipStream_t st);
+
+hipError_t launch_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, int log2bs,
+                                       const Code2Table &code, void *out, int out_dtype,
+                                       hipStream_t st);
+
 hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64_t K,
                                      const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
                                      int qt, void *dX, int dx_dtype, hipStream_t st);

@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_gemm_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
                                          ctypes.c_int, vp, ctypes.c_int, vp]),
+        "qmv_quantize_blockwise": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp, vp]),
+        "qmv_dequantize_blockwise": (ctypes.c_int, [vp, vp, i64, i32, vp, vp, ctypes.c_int, vp]),
         "qmv_gemm_4bit_backward": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
                                                   ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
@@ -239,6 +241,60 @@ def gemm_4bit(A: torch.Tensor, packed: torch.Tensor, state: QuantState,
               out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None):
     """C [M, N] = A [M, K] @ W_hat^T (A in bf16)."""
     return _matmul("gemm_4bit", A, packed, state, out, out_dtype)
+
+
+def _code8(code):
+    if code is None:
+        return None, None
+    buf = (ctypes.c_float * 256)(*[float(v) for v in code])
+    return ctypes.cast(buf, ctypes.c_void_p), buf
+
+
+def quantize_blockwise(A: torch.Tensor, blocksize: int = 4096, code: Optional[list] = None):
+    """8-bit blockwise codec: (q uint8 [numel], absmax fp32 [ceil(numel / blocksize)])."""
+    A = _dev(A, "A")
+    n = A.numel()
+    q = torch.empty(n, dtype=torch.uint8, device=A.device)
+    absmax = torch.empty(-(-n // blocksize), dtype=torch.float32, device=A.device)
+    cp, _keep = _code8(code)
+    _check(lib().qmv_quantize_blockwise(A.data_ptr(), _DT[A.dtype], n, blocksize, cp, q.data_ptr(),
+                                        absmax.data_ptr(), _stream(A)), "quantize_blockwise")
+    return q, absmax
+
+
+def dequantize_blockwise(q: torch.Tensor, absmax: torch.Tensor, blocksize: int = 4096,
+                         code: Optional[list] = None, out_dtype: torch.dtype = torch.float32,
+                         out: Optional[torch.Tensor] = None):
+    """out [numel] = code[q] * absmax[block], rounded to out_dtype."""
+    q = _dev(q, "q")
+    absmax = _dev(absmax, "absmax")
+    n = q.numel()
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=q.device)
+    elif not out.is_contiguous() or out.numel() != n or out.data_ptr() % 16:
+        raise ValueError("out must be contiguous, 16-byte aligned and hold numel elements")
+    cp, _keep = _code8(code)
+    _check(lib().qmv_dequantize_blockwise(q.data_ptr(), absmax.data_ptr(), n, blocksize, cp,
+                                          out.data_ptr(), _DT[out.dtype], _stream(q)),
+           "dequantize_blockwise")
+    return out
+
+
+def dynamic_tree_code() -> list:
+    """A signed dynamic-tree 8-bit table: a decimal exponent e = 0 .. 6 taken
+    by a run of leading zero bits, then 6 - e bits of linear fraction in
+    [0.1, 1] (bin centres), so each value is 10^-e * (0.1 + 0.9 (j + 1/2) /
+    2^(6 - e)); with their negatives, 0 and 1 that is 256 values, sorted."""
+    vals = {0.0, 1.0}
+    for e in range(7):
+        nf = 1 << (6 - e)
+        for j in range(nf):
+            v = float(torch.tensor(10.0 ** -e * (0.1 + 0.9 * (j + 0.5) / nf), dtype=torch.float32))
+            vals.add(v)
+            vals.add(-v)
+    out = sorted(vals)
+    assert len(out) == 256
+    return out
 
 
 def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState,

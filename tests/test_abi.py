@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(qmvlib, n), n
 
@@ -42,6 +42,8 @@ def test_code_tables_match_oracle_bits(qmvlib):
         assert got.view(np.uint32).tolist() == O.code_table(qt).view(np.uint32).tolist()
     got = np.array(qmv.default_code2(), dtype=np.float32)
     assert got.view(np.uint32).tolist() == O.linear8_table().view(np.uint32).tolist()
+    got = np.array(qmv.dynamic_tree_code(), dtype=np.float32)
+    assert got.view(np.uint32).tolist() == O.dynamic_tree_table().view(np.uint32).tolist()
 
 
 def test_status_strings(qmvlib):
@@ -142,3 +144,22 @@ def test_binding_refuses_cpu_tensors(qmvlib):
     import torch
     with pytest.raises(ValueError):
         qmv.quantize_4bit(torch.zeros(64))
+
+
+def test_blockwise_preconditions(qmvlib):
+    fq, fd = qmvlib.qmv_quantize_blockwise, qmvlib.qmv_dequantize_blockwise
+    assert fq(None, F32, 64, 64, None, P, P2, None) == INVALID
+    assert fq(P, F32, 0, 64, None, P, P2, None) == INVALID
+    assert fq(P, 9, 64, 64, None, P, P2, None) == INVALID
+    for bs in (16, 48, 8192, 0):
+        assert fq(P, BF16, 64, bs, None, P, P2, None) == UNSUPPORTED
+        assert fd(P, P2, 64, bs, None, P, F32, None) == UNSUPPORTED
+    assert fq(MIS, BF16, 64, 64, None, P, P2, None) == ALIGN
+    assert fq(P, BF16, 64, 64, None, P, MIS, None) == ALIGN
+    bad = (ctypes.c_float * 256)(*([0.0] * 256))                  # not increasing
+    assert fq(P, BF16, 64, 64, ctypes.cast(bad, ctypes.c_void_p), P, P2, None) == UNSUPPORTED
+    assert fd(P, P2, 64, 64, ctypes.cast(bad, ctypes.c_void_p), P, F32, None) == UNSUPPORTED
+    assert fd(None, P2, 64, 64, None, P, F32, None) == INVALID
+    assert fd(P, P2, -5, 64, None, P, F32, None) == INVALID
+    assert fd(P, P2, 64, 64, None, P, 3, None) == INVALID
+    assert fd(P, P2, 64, 64, None, MIS, BF16, None) == ALIGN

@@ -415,3 +415,127 @@ def test_quantize_full_pipeline_small_bf16_roundtrip():
     w = O.dequantize_4bit(packed, ahat, W.size, 64, "nf4").astype(np.float64)
     rel = np.linalg.norm(w - W) / np.linalg.norm(W)
     assert rel < 0.12
+
+
+# ---------------------------------------------------------------- 8-bit blockwise codec
+def _f32_nearest(q: Fraction) -> float:
+    """Correctly rounded fp32 of an exact rational (round to nearest even)."""
+    v = np.float32(float(q))
+    best = None
+    for c in (np.nextafter(v, np.float32(-np.inf)), v, np.nextafter(v, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - q)
+        key = (d, int(np.array(c, dtype=np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, float(c))
+    return best[1]
+
+
+def _decode_tree_byte(b: int) -> Fraction:
+    """Decode one byte of the dynamic-tree layout from its bits: sign, then a
+    run of e zero bits (the decimal exponent), a one bit, then 6 - e fraction
+    bits j selecting the centre of bin j of [0.1, 1] cut into 2^(6-e) bins.
+    The all-zero magnitude stands for 0 (positive sign) or 1 (negative sign)."""
+    sign, mag = b >> 7, b & 0x7F
+    if mag == 0:
+        return Fraction(1) if sign else Fraction(0)
+    e = 7 - mag.bit_length()            # leading zero bits of the 7-bit field
+    nf = 6 - e
+    j = mag & ((1 << nf) - 1)
+    centre = Fraction(1, 10) + Fraction(9, 10) * Fraction(2 * j + 1, 2 ** (nf + 1))
+    v = centre / Fraction(10) ** e
+    return -v if sign else v
+
+
+def test_dynamic_tree_table_from_bit_layout():
+    """Every byte decoded from the bit layout, rounded once to fp32, gives the
+    oracle's sorted table exactly; decades hold 64, 32, ..., 1 values."""
+    t = O.dynamic_tree_table()
+    want = sorted(_f32_nearest(_decode_tree_byte(b)) for b in range(256))
+    assert t.dtype == np.float32 and t.size == 256
+    assert t.tolist() == want
+    assert np.all(np.diff(t) > 0)
+    pos = t[t > 0]
+    assert pos.max() == 1.0 and np.array_equal(np.sort(-t[t < 0]), pos[pos < 1])
+    for e in range(7):
+        lo, hi = 0.1 * 10.0 ** -e, 10.0 ** -e
+        assert int(((pos > lo) & (pos < hi)).sum()) == 2 ** (6 - e)
+
+
+def _frac_table(table):
+    return [Fraction(float(v)) for v in table]
+
+
+def _frac_nearest_fast(x: float, a: float, ftab) -> int:
+    n = Fraction(0) if a == 0 else Fraction(x) / Fraction(a)
+    return min(range(len(ftab)), key=lambda c: (abs(n - ftab[c]), abs(ftab[c]), c))
+
+
+@pytest.mark.parametrize("table", ["linear", "dynamic"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_blockwise_codes_match_rational_bruteforce(table, dtype):
+    rng = np.random.default_rng(21)
+    n, bs = 600, 128                      # four full blocks and a ragged one
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    x = torch.from_numpy(rng.standard_normal(n) * np.repeat(10.0 ** rng.uniform(-3, 1, 5), bs)[:n])
+    x = x.to(tdt).to(torch.float64).numpy()
+    x[130:140] = 0.0                       # zeros inside a live block
+    code = O.linear8_table() if table == "linear" else O.dynamic_tree_table()
+    q, absmax = O.quantize_blockwise(x, bs, code)
+    assert q.dtype == np.uint8 and absmax.dtype == np.float32 and absmax.size == 5
+    for b in range(5):
+        assert float(absmax[b]) == float(np.max(np.abs(x[b * bs:(b + 1) * bs])))
+    ftab = _frac_table(code)
+    want = [_frac_nearest_fast(float(x[i]), float(absmax[i // bs]), ftab) for i in range(n)]
+    assert q.tolist() == want
+
+
+def test_blockwise_exact_ties_and_extremes():
+    """Midpoints of adjacent dynamic-tree values, scaled by an exact power of
+    two, sit exactly on the tie and go to the smaller magnitude; the block's
+    largest positive element takes the code of 1."""
+    t = O.dynamic_tree_table()
+    mids = (t[:-1].astype(np.float64) + t[1:].astype(np.float64)) / 2.0
+    a = 4.0
+    x = np.concatenate([[a], mids * a])          # first element fixes absmax = a
+    q, absmax = O.quantize_blockwise(x, x.size, t)
+    assert absmax.tolist() == [a] and t[q[0]] == 1.0
+    for k in range(mids.size):
+        lo, hi = k, k + 1
+        assert q[k + 1] == (lo if abs(t[lo]) < abs(t[hi]) else hi)
+
+
+def test_blockwise_zero_block_and_roundtrip_bound():
+    rng = np.random.default_rng(5)
+    bs = 256
+    x = rng.standard_normal(bs * 6 + 77) * 0.3
+    x[bs:2 * bs] = 0.0
+    for code in (O.linear8_table(), O.dynamic_tree_table()):
+        q, absmax = O.quantize_blockwise(x, bs, code)
+        zero = int(np.flatnonzero(code == 0)[0])
+        assert absmax[1] == 0 and np.all(q[bs:2 * bs] == zero)
+        w = O.dequantize_blockwise(q, absmax, bs, code)
+        assert w.dtype == np.float32 and np.all(w[bs:2 * bs] == 0)
+        # |x / absmax| <= 1, so the error is at most absmax times the larger of
+        # half the widest gap and the distance from +-1 to the table's ends,
+        # plus the final fp32 rounding of w
+        c64 = code.astype(np.float64)
+        reach = max(np.max(np.diff(c64)) / 2, 1 - c64.max(), 1 + c64.min())
+        a_el = np.repeat(absmax.astype(np.float64), bs)[: x.size]
+        assert np.all(np.abs(w - x) <= reach * a_el + np.abs(w) * 2.0 ** -24)
+
+
+def test_dequantize_blockwise_is_one_fp32_rounding():
+    rng = np.random.default_rng(8)
+    bs = 64
+    q = rng.integers(0, 256, bs * 30 + 9).astype(np.uint8)
+    absmax = (np.abs(rng.standard_normal(31)) * 3.0).astype(np.float32)
+    t = O.dynamic_tree_table()
+    w = O.dequantize_blockwise(q, absmax, bs, t)
+    for i in range(0, q.size, 7):
+        exact = Fraction(float(t[q[i]])) * Fraction(float(absmax[i // bs]))
+        assert float(w[i]) == _f32_nearest(exact)
+    wb = O.dequantize_blockwise(q, absmax, bs, t, "bf16")
+    tb = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(wb, tb)
+    wh = O.dequantize_blockwise(q, absmax, bs, t, "fp16")
+    assert np.array_equal(np.asarray(wh).view(np.uint16), w.astype(np.float16).view(np.uint16))
