@@ -66,26 +66,6 @@ __device__ __forceinline__ float threshold_f32(double p, bool pos) {
   return __uint_as_float(pos ? rd : f32_step_down_bits(__uint_as_float(ru)));
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
-}
-
-// Max over aligned groups of G lanes (G a power of two, uniform) of a
-// non-negative float, compared as unsigned bits (same order, and no NaN
-// canonicalisation around each step): DPP moves inside rows of 16 lanes,
-// lane shuffles beyond.
-__device__ __forceinline__ float group_max(float m, int G) {
-  uint32_t u = __float_as_uint(m);
-  if (G >= 2) u = max(u, dpp_u32<0xb1>(u));   // quad_perm [1,0,3,2]
-  if (G >= 4) u = max(u, dpp_u32<0x4e>(u));   // quad_perm [2,3,0,1]
-  if (G >= 8) u = max(u, dpp_u32<0x141>(u));  // row_half_mirror
-  if (G >= 16) u = max(u, dpp_u32<0x140>(u)); // row_mirror
-  if (G >= 32) u = max(u, (uint32_t)__shfl_xor((int)u, 16));
-  if (G >= 64) u = max(u, (uint32_t)__shfl_xor((int)u, 32));
-  return __uint_as_float(u);
-}
-
 // Rank among the thresholds (0..15 for NF4, 0..14 for FP4) -> code.
 template <int QT>
 __device__ __forceinline__ uint32_t rank_to_code(int r) {
@@ -648,12 +628,8 @@ __device__ __forceinline__ float fused_offset(const double *__restrict__ levels,
   return (float)__ddiv_rn(total, (double)n);
 }
 
-//
-// The same kernel is the 8-bit blockwise codec (quantize_blockwise): DT is the
-// input type (fp32 for the scales) and ZOFF drops the offset (c = x), so the
-// group max is the block absmax and q the nearest code of x / absmax.
-template <int E, int DT, bool ZOFF>
-__global__ __launch_bounds__(256) void dq_encode_kernel(const void *__restrict__ absmax_v,
+template <int E>
+__global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict__ absmax,
                                                         int64_t n, int log2bs2, Code2Table code2,
                                                         int linear, const double *__restrict__ levels,
                                                         const int2 *__restrict__ stats, int64_t nl,
@@ -661,8 +637,6 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const void *__restrict__
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ absmax2,
                                                         float *__restrict__ code2_out) {
-  using T = typename Storage<DT>::type;
-  const T *absmax = static_cast<const T *>(absmax_v);
   __shared__ double mid[256];
   __shared__ float wave_max[4];
   __shared__ double red[kTopFused / kFanIn];
@@ -672,9 +646,7 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const void *__restrict__
   if (tid < 255) mid[tid] = ((double)code2.v[tid] + (double)code2.v[tid + 1]) * 0.5;  // exact
   if (code2_out && blockIdx.x == 0) code2_out[tid] = code2.v[tid];
   float off;
-  if (ZOFF) {
-    off = 0.f;
-  } else if (nl > 1 && nl <= kTopFused) {
+  if (nl > 1 && nl <= kTopFused) {
     off = fused_offset(levels, nl, stats, n, red);
     if (blockIdx.x == 0 && tid == 0) offset[0] = off;
   } else {
@@ -691,17 +663,12 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const void *__restrict__
     // the tile's scales through a range-limited buffer: no branch per load
     const int64_t rem = n - t * tile;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(absmax + t * tile, (uint32_t)((rem < tile ? rem : tile) * sizeof(T)));
+        make_rsrc(absmax + t * tile, (uint32_t)((rem < tile ? rem : tile) * sizeof(float)));
     float a[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if constexpr (DT == kF32)
-        a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             rs, (uint32_t)((tid * E + e) * 4), 0, 0));
-      else
-        a[e] = bits16_to_f32<DT>((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-            rs, (uint32_t)((tid * E + e) * 2), 0, 0));
-    }
+    for (int e = 0; e < E; ++e)
+      a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, (uint32_t)((tid * E + e) * 4), 0, 0));
     float c[E];
     float m = 0.f;
 #pragma unroll
@@ -731,19 +698,34 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const void *__restrict__
     };
     int code[E];
     if (linear) {
-      // first guess k ~ 127 c / m in fp32 (the exact thresholds below fix it
-      // by one step); a block with a tiny max is first scaled up by an exact
-      // 2^64 so that 127 / m stays finite
+      // y = fp32(127 n + 127), n = c / m, and k = rint(y) saturated to
+      // 0 .. 255 (|n| <= 1, so k <= 254; a group with a tiny max is scaled up
+      // by an exact 2^64 so that 127 / m stays finite).  y is within 2.3e-5
+      // of the exact 127 n + 127 (the reciprocal's and the fma's roundings)
+      // and each threshold 127 mid_j + 127 within 3.9e-6 of j + 1/2, so when
+      // y is more than 2^-13 inside the half-integers around k, k is the
+      // code; otherwise k is within one of it and two exact comparisons
+      // settle it.
       const float up = m < 0x1p-60f ? 0x1p64f : 1.f;
       const float inv = m > 0.f ? 127.f / (m * up) : 0.f;
+      uint32_t unsure = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        int k = (int)rintf((c[e] * up) * inv) + 127;
-        k = k < 0 ? 0 : (k > 254 ? 254 : k);  // code 255 (> 1) is never nearest
-        const double x = (double)c[e];
-        k += (k < 255 && above(x, k)) ? 1 : 0;
-        k -= (k > 0 && !above(x, k - 1)) ? 1 : 0;
-        code[e] = k;
+        const float y = fmaf(c[e] * up, inv, 127.f);
+        code[e] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y, 0, 0u);
+        unsure |= fabsf(y - (float)code[e]) < 0.5f - 0x1p-13f ? 0u : (1u << e);
+      }
+      if (__builtin_amdgcn_ballot_w64(unsure != 0) != 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (unsure & (1u << e)) {
+            int k = code[e];
+            const double x = (double)c[e];
+            k += (k < 255 && above(x, k)) ? 1 : 0;
+            k -= (k > 0 && !above(x, k - 1)) ? 1 : 0;
+            code[e] = k;
+          }
+        }
       }
     } else {
       int lo[E], hi[E];
@@ -805,97 +787,11 @@ hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2
   const int64_t ntiles = (nblocks + tile - 1) / tile;
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
 #define QMV_E(EV)                                                                          \
-  hipLaunchKernelGGL((dq_encode_kernel<EV, kF32, false>), dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
+  hipLaunchKernelGGL((dq_encode_kernel<EV>), dim3(grid), dim3(256), 0, st, absmax, nblocks, log2bs2, \
                      code2, linear ? 1 : 0, levels, stats, runs > kTopFused ? (int64_t)1 : runs, \
                      offset, q, absmax2, code2_out)
   if (E == 8) QMV_E(8); else QMV_E(16);
 #undef QMV_E
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// 8-bit blockwise codec ("Feat/mps gemm 4bit bf16", table "What runs natively
-// now": quantize_blockwise / dequantize_blockwise; "Known failures": the
-// exact float64 nearest-code search is the reference).
-// ---------------------------------------------------------------------------
-hipError_t launch_quantize_blockwise(const void *A, int a_dtype, int64_t n, int log2bs,
-                                     const Code2Table &code, bool linear, uint8_t *q,
-                                     float *absmax, hipStream_t st) {
-  const int bs = 1 << log2bs;
-  const int E = bs > 2048 ? 16 : 8;
-  const int64_t tile = 256 * (int64_t)E;
-  const int64_t ntiles = (n + tile - 1) / tile;
-  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, 1 << 16);
-#define QMV_QB(EV, DTV)                                                                            \
-  hipLaunchKernelGGL((dq_encode_kernel<EV, DTV, true>), dim3(grid), dim3(256), 0, st, A, n, log2bs, \
-                     code, linear ? 1 : 0, nullptr, nullptr, (int64_t)1, nullptr, q, absmax, nullptr)
-#define QMV_QBD(EV)                                \
-  if (a_dtype == kF32) { QMV_QB(EV, kF32); }       \
-  else if (a_dtype == kF16) { QMV_QB(EV, kF16); }  \
-  else { QMV_QB(EV, kBF16); }
-  if (E == 8) { QMV_QBD(8); } else { QMV_QBD(16); }
-#undef QMV_QBD
-#undef QMV_QB
-  return hipGetLastError();
-}
-
-// out[i] = fp32(code[q[i]] * absmax[i / blocksize]) rounded to the output
-// type; 16 codes per thread (one 16-byte load, one block: blocks are >= 32).
-template <int ODT>
-__global__ __launch_bounds__(256) void dequantize_blockwise_kernel(const uint8_t *__restrict__ q,
-                                                                   const float *__restrict__ absmax,
-                                                                   int64_t n, int log2bs,
-                                                                   Code2Table code, void *out_v) {
-  using OT = typename Storage<ODT>::type;
-  OT *out = static_cast<OT *>(out_v);
-  __shared__ float tab[256];
-  tab[threadIdx.x] = code.v[threadIdx.x];
-  __syncthreads();
-  const int64_t chunks = (n + 15) / 16;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
-    const int64_t i0 = c * 16;
-    const float a = absmax[i0 >> log2bs];
-    if (i0 + 16 <= n) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(q + i0);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      float v[16];
-#pragma unroll
-      for (int b = 0; b < 16; ++b) v[b] = materialize(tab[(ws[b >> 2] >> (8 * (b & 3))) & 0xffu] * a);
-      if constexpr (ODT == kF32) {
-        uint4 *dst = reinterpret_cast<uint4 *>(out + i0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          dst[k] = make_uint4(__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                              __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3]));
-      } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          h[k] = f32_to_bits16<ODT>(v[2 * k]) | (f32_to_bits16<ODT>(v[2 * k + 1]) << 16);
-        uint4 *dst = reinterpret_cast<uint4 *>(out + i0);
-        dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
-        dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
-      }
-    } else {
-      for (int64_t i = i0; i < n; ++i) store_elem<ODT>(out, i, materialize(tab[q[i]] * a));
-    }
-  }
-}
-
-hipError_t launch_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, int log2bs,
-                                       const Code2Table &code, void *out, int out_dtype,
-                                       hipStream_t st) {
-  const int64_t chunks = (n + 15) / 16;
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, 8 * device_cu_count()));
-  if (out_dtype == kF32)
-    hipLaunchKernelGGL(dequantize_blockwise_kernel<kF32>, dim3(grid), dim3(256), 0, st, q, absmax, n,
-                       log2bs, code, out);
-  else if (out_dtype == kF16)
-    hipLaunchKernelGGL(dequantize_blockwise_kernel<kF16>, dim3(grid), dim3(256), 0, st, q, absmax, n,
-                       log2bs, code, out);
-  else
-    hipLaunchKernelGGL(dequantize_blockwise_kernel<kBF16>, dim3(grid), dim3(256), 0, st, q, absmax, n,
-                       log2bs, code, out);
   return hipGetLastError();
 }
 
@@ -934,20 +830,6 @@ hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t n, float 
 // once to fp32 and then converted (bf16: v_cvt_pk_bf16_f32, round to nearest
 // even).  Elements past the last full chunk are written by the tail loop.
 // ---------------------------------------------------------------------------
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v_t;
-
-template <int ODT>
-__device__ __forceinline__ uint32_t cvt_pair(float lo, float hi) {
-  if constexpr (ODT == kBF16) {
-    const f32x2_t v = {materialize(lo), materialize(hi)};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
-  } else {
-    return f32_to_f16_rne(lo) | (f32_to_f16_rne(hi) << 16);
-  }
-}
-
 constexpr int kDeqThreads = 256;
 constexpr int kDeqU = 2;  // chunks in flight per wave
 

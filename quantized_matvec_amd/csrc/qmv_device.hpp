@@ -123,4 +123,39 @@ __device__ __forceinline__ void store_elem(typename Storage<DT>::type *p, int64_
   else p[i] = (uint16_t)f32_to_bits16<DT>(v);
 }
 
+// Lane moves and lane-group reductions.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+// Max over aligned groups of G lanes (G a power of two, uniform) of a
+// non-negative float, compared as unsigned bits (same order, and no NaN
+// canonicalisation around each step): DPP moves inside rows of 16 lanes,
+// lane shuffles beyond.
+__device__ __forceinline__ float group_max(float m, int G) {
+  uint32_t u = __float_as_uint(m);
+  if (G >= 2) u = max(u, dpp_u32<0xb1>(u));   // quad_perm [1,0,3,2]
+  if (G >= 4) u = max(u, dpp_u32<0x4e>(u));   // quad_perm [2,3,0,1]
+  if (G >= 8) u = max(u, dpp_u32<0x141>(u));  // row_half_mirror
+  if (G >= 16) u = max(u, dpp_u32<0x140>(u)); // row_mirror
+  if (G >= 32) u = max(u, (uint32_t)__shfl_xor((int)u, 16));
+  if (G >= 64) u = max(u, (uint32_t)__shfl_xor((int)u, 32));
+  return __uint_as_float(u);
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v_t;
+
+template <int ODT>
+__device__ __forceinline__ uint32_t cvt_pair(float lo, float hi) {
+  if constexpr (ODT == kBF16) {
+    const f32x2_t v = {materialize(lo), materialize(hi)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+  } else {
+    return f32_to_f16_rne(lo) | (f32_to_f16_rne(hi) << 16);
+  }
+}
+
 }  // namespace qmv
