@@ -41,26 +41,27 @@ namespace qmv {
 //
 // First guess of the code, from the fp32 approximation n ~ x / absmax:
 //   linear table (k - 127) / 127: rint(127 n) + 127;
-//   any other table: a 4224-entry byte table indexed by the sign, the binade
-//   (2^-32 .. 2^0, clamped) and the top six fraction bits of n, holding the
-//   number of midpoints below the lower edge of that range.
+//   any other table: n is placed in one of 4224 ranges by its sign, binade
+//   (2^-32 .. 2^0, clamped) and top six fraction bits (qb_key).  Widened by
+//   the error of n, a range holds g midpoints below it and, for nearly every
+//   range of nearly every table, at most one inside it (QbRange).
 // Linear table: the guess is the code unless 127 n + 127 is within a small
 // guard of a half-integer (bound below); then the guess k is within one of
 // the code, and the code is k - 1 + [x above threshold k - 1] + [x above
-// threshold k].  Other tables: three independent comparisons around the
-// guess g settle every code in {g, g + 1} (a range of n holds at most one
-// midpoint for most tables); otherwise the guess is moved one threshold at a
-// time.
+// threshold k].  Other tables: the code is g, or g + [n > the range's
+// midpoint] when n is clearly away from it; elements near a midpoint, and
+// ranges holding several, take the exact search.
 // ---------------------------------------------------------------------------
 constexpr int kQbTile = 4096;
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-// Linear table: the fp32 y = fma(x up, fp32(127 / (absmax up)), 127) differs
-// from the exact 127 n + 127 by at most 127 2^-24 (the reciprocal) plus
-// 255 2^-24 (the fma), under 2.3e-5; each threshold 127 mid_j + 127 lies
-// within 127 2^-25 < 3.9e-6 of j + 1/2 (table values are (j - 127) / 127
-// rounded to fp32).  When y is more than 2^-13 (> 2.7e-5) inside the
-// half-integers around rint(y), every threshold is strictly on its side of
-// the exact value, and rint(y) is the code.
+// Linear table: y = fma(x, fp32(127 rcp(absmax)), 127) in fp32 differs from
+// the exact 127 n + 127 by at most 127 (2^-23 + 2^-24) (the reciprocal, 1 ulp,
+// and the product) plus 2^-17 (the fma), under 3.1e-5; each threshold
+// 127 mid_j + 127 lies within 127 2^-25 < 3.9e-6 of j + 1/2 (table values are
+// (j - 127) / 127 rounded to fp32).  When y is more than 2^-13 (1.2e-4)
+// inside the half-integers around rint(y), every threshold is strictly on its
+// side of the exact value, and rint(y) is the code.
 constexpr float kLinGuard = 0x1p-13f;
 constexpr int kQbSub = 6;          // fraction bits of n in the key
 constexpr int kQbHalf = 33 << kQbSub;  // keys per sign: 33 binades x 64 sub-ranges
@@ -72,7 +73,7 @@ __device__ __forceinline__ int qb_key(float n) {
   const uint32_t u = __float_as_uint(n);
   int i = (int)((u & 0x7fffffffu) >> (23 - kQbSub)) - kQbBin0;
   i = i < 0 ? 0 : (i > kQbHalf - 1 ? kQbHalf - 1 : i);
-  return (u >> 31) ? kQbHalf - 1 - i : kQbHalf + i;
+  return kQbHalf + (i ^ ((int)u >> 31));  // negative: kQbHalf - 1 - i
 }
 
 // Lower edge of the range of n that maps to key k.
@@ -84,6 +85,20 @@ __device__ __forceinline__ double qb_key_low(int k) {
   const int i = kQbHalf - 1 - k;
   return -(double)__uint_as_float((uint32_t)(i + 1 + kQbBin0) << (23 - kQbSub));
 }
+
+// One range of n for tables other than the linear one (n' = x * rcp(absmax)
+// in fp32 is within 2^-22 of n, relative): g = number of midpoints under the
+// range widened by 2^-20 of its edges; hi = the top of an interval of doubt
+// [hi - 2^-17 |hi|, hi] that covers mf -+ 2^-18 |mf|, mf the one midpoint
+// inside the widened range rounded to fp32 (n' outside it is on the same
+// side of mf as n is of the exact midpoint: both errors together are under
+// 2^-21 |mf|); hi = FLT_MAX when the range holds no midpoint (n' is always
+// below), NaN when it holds several (and for the range around zero when it
+// holds any: there n' may be subnormal, without a relative bound).
+struct alignas(8) QbRange {
+  float hi;
+  int g;
+};
 
 // One threshold of the search: the midpoint and its tie bias (see above).
 struct alignas(16) QbThr {
@@ -103,10 +118,10 @@ __device__ __attribute__((noinline)) int qb_search(const QbThr *th, double x, do
   return k;
 }
 
-template <int DT>
+template <int DT, bool LIN>
 __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__restrict__ Av,
                                                                  int64_t n, int log2bs,
-                                                                 Code2Table code, int linear,
+                                                                 Code2Table code,
                                                                  uint8_t *__restrict__ q,
                                                                  float *__restrict__ absmax) {
   using T = typename Storage<DT>::type;
@@ -116,10 +131,10 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
   // thresholds 0 .. 254 at th_s[1 ..]; th_s[0] (-inf: every x with absmax > 0
   // is above it) and th_s[256], th_s[257] (+inf: none is) bound the search
   __shared__ QbThr th_s[258];
-  __shared__ uint8_t guess[kQbKeys];
+  __shared__ QbRange ranges[LIN ? 1 : kQbKeys];
   // two sets, used by alternate tiles: a set is rewritten only after every
   // thread has passed the next tile's barrier
-  __shared__ float wave_max[2][R][4];
+  __shared__ uint32_t wave_max[2][R][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -131,16 +146,52 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
     if (tid == 1) th_s[257] = QbThr{INFINITY, 0.0};
   }
   __syncthreads();
-  if (!linear) {
-    for (int k = tid; k < kQbKeys; k += 256) {
-      const double lo = qb_key_low(k);
-      int a = 0, b = 255;  // number of midpoints below lo, by bisection
-      while (a < b) {
-        const int md = (a + b) >> 1;
-        if (th[md].mid < lo) a = md + 1;
-        else b = md;
+  if constexpr (!LIN) {
+    // thread t fills ranges [17 t, 17 t + 17): one bisection for the first
+    // range's counts, then both counts only move up (the widened edges grow
+    // with the key); th[255].mid = +inf stops the walks
+    constexpr int kPer = (kQbKeys + 255) / 256;
+    const int k0 = tid * kPer;
+    const int k1 = k0 + kPer < kQbKeys ? k0 + kPer : kQbKeys;
+    int g = 0, h = 0;
+    for (int k = k0; k < k1; ++k) {
+      const bool pos = k >= kQbHalf;
+      const int i = pos ? k - kQbHalf : kQbHalf - 1 - k;  // |n| sub-range
+      const double a0 = i == 0 ? 0.0 : (double)__uint_as_float((uint32_t)(i + kQbBin0) << (23 - kQbSub));
+      const double a1 = (double)__uint_as_float((uint32_t)(i + 1 + kQbBin0) << (23 - kQbSub));
+      const double lo = pos ? a0 * (1.0 - 0x1p-20) : -a1 * (1.0 + 0x1p-20);
+      const double hi = pos ? a1 * (1.0 + 0x1p-20) : -a0 * (1.0 - 0x1p-20);
+      if (k == k0) {
+        int a = 0, b = 255;
+        while (a < b) {  // midpoints < lo
+          const int md = (a + b) >> 1;
+          if (th[md].mid < lo) a = md + 1;
+          else b = md;
+        }
+        g = a;
+        a = g, b = 255;
+        while (a < b) {  // midpoints <= hi
+          const int md = (a + b) >> 1;
+          if (th[md].mid <= hi) a = md + 1;
+          else b = md;
+        }
+        h = a;
+      } else {
+        while (th[g].mid < lo) ++g;
+        if (h < g) h = g;
+        while (th[h].mid <= hi) ++h;
       }
-      guess[k] = (uint8_t)a;
+      const int inside = h - g;
+      float hi_d;
+      if (inside == 0) {
+        hi_d = 3.4028234663852886e38f;  // n' is always below the interval
+      } else if (inside == 1 && i != 0) {
+        const float mf = (float)th[g].mid;
+        hi_d = mf + fabsf(mf) * 0x1p-18f;  // the interval covers mf -+ 2^-18 |mf|
+      } else {
+        hi_d = __builtin_nanf("");  // never decided
+      }
+      ranges[k] = QbRange{hi_d, g};
     }
     __syncthreads();
   }
@@ -171,84 +222,128 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
     }
   };
 
-  auto process = [&](int64_t t, const float (&v)[R][VE], int par, auto full_tag) {
+  // per-load max |x| as fp32 bits (non-negative floats order as their bits;
+  // integer maxima also skip the NaN quieting a float max needs)
+  auto local_max_raw = [&](const uint4 (&raw)[R], uint32_t (&mb)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+      if constexpr (DT == kF32) {
+        mb[r] = max(max(w[0] & 0x7fffffffu, w[1] & 0x7fffffffu),
+                    max(w[2] & 0x7fffffffu, w[3] & 0x7fffffffu));
+      } else {
+        u16x2_t acc = __builtin_bit_cast(u16x2_t, w[0] & 0x7fff7fffu);
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+          acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2_t, w[i] & 0x7fff7fffu));
+        mb[r] = __float_as_uint(bits16_to_f32<DT>(max((uint32_t)acc.x, (uint32_t)acc.y)));
+      }
+    }
+  };
+
+  auto process = [&](int64_t t, const float (&v)[R][VE], const uint32_t (&mb)[R], int par,
+                     auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t base = t * kQbTile;
     float m[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float mm = 0.f;
-#pragma unroll
-      for (int j = 0; j < VE; ++j) mm = fmaxf(mm, fabsf(v[r][j]));
-      m[r] = group_max(mm, G < 64 ? G : 64);
-    }
+    for (int r = 0; r < R; ++r) m[r] = group_max(__uint_as_float(mb[r]), G < 64 ? G : 64);
     if (G > 64) {  // uniform across the launch
       if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) wave_max[par][r][wave] = m[r];
+        for (int r = 0; r < R; ++r) wave_max[par][r][wave] = __float_as_uint(m[r]);
       }
       __syncthreads();
-      const int wpb = G >= 256 ? 4 : G >> 6;  // waves of a block within one load
-      const int w0 = (wave / wpb) * wpb;
-      const int lpb = G > 256 ? G >> 8 : 1;   // loads a block spans
+      if (G >= 256) {  // a block covers whole loads: all four waves, lpb loads
+        uint32_t wm[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int r0 = (r / lpb) * lpb;
-        float mm = 0.f;
-        for (int rr = r0; rr < r0 + lpb; ++rr)
-          for (int w = w0; w < w0 + wpb; ++w) mm = fmaxf(mm, wave_max[par][rr][w]);
-        m[r] = mm;
+        for (int r = 0; r < R; ++r)
+          wm[r] = max(max(wave_max[par][r][0], wave_max[par][r][1]),
+                      max(wave_max[par][r][2], wave_max[par][r][3]));
+        const int lpb = G >> 8;  // 1, 2 or 4 (4 only when R == 4)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          uint32_t mm = wm[r];
+          if (lpb >= 2) mm = max(mm, wm[r ^ 1]);
+          if constexpr (R == 4) {
+            if (lpb == 4) mm = max(mm, max(wm[r ^ 2], wm[r ^ 3]));
+          }
+          m[r] = __uint_as_float(mm);
+        }
+      } else {  // two waves per block
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          m[r] = __uint_as_float(max(wave_max[par][r][wave], wave_max[par][r][wave ^ 1]));
       }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t e0 = base + r * 256 * VE + tid * VE;
       if ((e0 & (bs - 1)) == 0 && (FULL || e0 < n)) absmax[e0 >> log2bs] = m[r];
-      const double sd = (double)m[r];
+      const float mr = m[r];
+      const double sd = (double)mr;
       int c[VE];
-      // n ~ x / absmax is formed as (x up) / (absmax up): tiny maxima are
-      // scaled up by an exact 2^64 so the reciprocal stays finite
-      const float up = m[r] < 0x1p-60f ? 0x1p64f : 1.f;
-      if (linear) {
+      // the fast guess uses an fp32 reciprocal of absmax (absmax >= 2^-120;
+      // NaN below, which sends the group to the exact path; 0 for a zero block)
+      const float rc = mr == 0.f ? 0.f : (mr >= 0x1p-120f ? __builtin_amdgcn_rcpf(mr) : __builtin_nanf(""));
+      // exact path: n from (x up) / (absmax up), tiny maxima scaled up by an
+      // exact 2^64 so that the reciprocal stays finite
+      const float up = mr < 0x1p-60f ? 0x1p64f : 1.f;
+      if constexpr (LIN) {
         // y = fp32(127 n + 127) and k = rint(y), saturated to 0 .. 255 by the
         // conversion (|n| <= 1, so k <= 254).  k is the code unless y lies
-        // within kLinGuard of a half-integer; such elements take the exact
-        // two-threshold check (the code is k - 1, k or k + 1)
-        const float inv = m[r] > 0.f ? 127.f / (m[r] * up) : 0.f;
-        uint32_t unsure = 0;
+        // within kLinGuard of a half-integer: then only the threshold between
+        // floor(y) and floor(y) + 1 is near, and one exact comparison settles
+        // the code.  A NaN y (absmax below 2^-120) takes the scaled path.
+        const float inv = 127.f * rc;
+        float y[VE];
+        bool any = false;
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
-          const float y = fmaf(v[r][j] * up, inv, 127.f);
-          c[j] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y, 0, 0u);
-          unsure |= fabsf(y - (float)c[j]) < 0.5f - kLinGuard ? 0u : (1u << j);
+          y[j] = fmaf(v[r][j], inv, 127.f);
+          c[j] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y[j], 0, 0u);
+          any |= !(fabsf(y[j] - (float)c[j]) < 0.5f - kLinGuard);
         }
-        if (__builtin_amdgcn_ballot_w64(unsure != 0) != 0) {
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
           for (int j = 0; j < VE; ++j) {
-            if (unsure & (1u << j)) {
-              const int k = c[j];
+            const float d = y[j] - (float)c[j];
+            const bool u = !(fabsf(d) < 0.5f - kLinGuard);
+            if (__builtin_amdgcn_ballot_w64(u) != 0 && u) {
               const double x = (double)v[r][j];
-              c[j] = k - 1 + (qb_above(th[k - 1], x, sd) ? 1 : 0) + (qb_above(th[k], x, sd) ? 1 : 0);
+              if (mr >= 0x1p-120f) {
+                const int kf = c[j] - (d < 0.f ? 1 : 0);  // th[-1] is -inf
+                c[j] = kf + (qb_above(th[kf], x, sd) ? 1 : 0);
+              } else {  // tiny absmax: k from a correctly rounded 127 / (absmax up)
+                const int k = (int)__builtin_amdgcn_cvt_pk_u8_f32(
+                    fmaf(v[r][j] * up, 127.f / (mr * up), 127.f), 0, 0u);
+                c[j] = k - 1 + (qb_above(th[k - 1], x, sd) ? 1 : 0) + (qb_above(th[k], x, sd) ? 1 : 0);
+              }
             }
           }
         }
       } else {
-        const float inv = m[r] > 0.f ? __builtin_amdgcn_rcpf(m[r] * up) : 0.f;
-        uint32_t slow = 0;
+        // the code is g, or g + 1 when n' is above the range's interval of
+        // doubt [hi - 2^-17 |hi|, hi]; n' inside it (or a NaN range) takes the
+        // exact search
+        float nn[VE];
+        bool any = false;
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
-          const int k = guess[qb_key((v[r][j] * up) * inv)];
-          const double x = (double)v[r][j];
-          const bool lo = qb_above(th[k - 1], x, sd);
-          const bool at = qb_above(th[k], x, sd);
-          const bool hi = qb_above(th[k + 1], x, sd);  // th[255], th[256]: +inf
-          c[j] = k + (at ? 1 : 0);
-          slow |= (lo && !hi) ? 0u : (1u << j);  // the code is not k or k + 1
+          nn[j] = v[r][j] * rc;
+          const QbRange e = ranges[qb_key(nn[j])];
+          c[j] = e.g + (nn[j] > e.hi ? 1 : 0);
+          any |= !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-17f, fabsf(e.hi), e.hi));
         }
-        if (__builtin_amdgcn_ballot_w64(slow != 0) != 0) {
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+          const float rc2 = mr > 0.f ? __builtin_amdgcn_rcpf(mr * up) : 0.f;
 #pragma unroll
-          for (int j = 0; j < VE; ++j)
-            if (slow & (1u << j)) c[j] = qb_search(th, (double)v[r][j], sd, c[j]);
+          for (int j = 0; j < VE; ++j) {
+            const QbRange e = ranges[qb_key(nn[j])];
+            const bool u = !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-17f, fabsf(e.hi), e.hi));
+            if (__builtin_amdgcn_ballot_w64(u) != 0 && u)
+              c[j] = qb_search(th, (double)v[r][j], sd, ranges[qb_key((v[r][j] * up) * rc2)].g);
+          }
         }
       }
       uint32_t word[VE / 4];
@@ -276,10 +371,12 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
     load_full(t < nfull ? t : nfull - 1, nx);
     for (; t < nfull; t += gridDim.x) {
       float v[R][VE];
+      uint32_t mb[R];
       convert(nx, v);
+      local_max_raw(nx, mb);
       const int64_t tn = t + gridDim.x;
       load_full(tn < nfull ? tn : nfull - 1, nx);
-      process(t, v, par, std::true_type{});
+      process(t, v, mb, par, std::true_type{});
       par ^= 1;
     }
   }
@@ -294,25 +391,43 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
         const int64_t e = base + r * 256 * VE + tid * VE + j;
         v[r][j] = e < n ? load_elem<DT>(A, e) : 0.f;
       }
-    process(t, v, par, std::false_type{});
+    uint32_t mb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t mm = 0;
+#pragma unroll
+      for (int j = 0; j < VE; ++j) mm = max(mm, __float_as_uint(v[r][j]) & 0x7fffffffu);
+      mb[r] = mm;
+    }
+    process(t, v, mb, par, std::false_type{});
   }
+}
+
+template <int DT>
+static void launch_qb_t(int64_t ntiles, const void *A, int64_t n, int log2bs, const Code2Table &code,
+                        bool linear, uint8_t *q, float *absmax, hipStream_t st) {
+  // one resident generation of workgroups, each striding over the tiles
+  static const int occ_lin = resident_wgs_per_cu(
+      reinterpret_cast<const void *>(&quantize_blockwise_kernel<DT, true>), 256);
+  static const int occ_gen = resident_wgs_per_cu(
+      reinterpret_cast<const void *>(&quantize_blockwise_kernel<DT, false>), 256);
+  const int64_t slots = (int64_t)device_cu_count() * (linear ? occ_lin : occ_gen);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, slots));
+  if (linear)
+    hipLaunchKernelGGL((quantize_blockwise_kernel<DT, true>), dim3(grid), dim3(256), 0, st, A, n,
+                       log2bs, code, q, absmax);
+  else
+    hipLaunchKernelGGL((quantize_blockwise_kernel<DT, false>), dim3(grid), dim3(256), 0, st, A, n,
+                       log2bs, code, q, absmax);
 }
 
 hipError_t launch_quantize_blockwise(const void *A, int a_dtype, int64_t n, int log2bs,
                                      const Code2Table &code, bool linear, uint8_t *q,
                                      float *absmax, hipStream_t st) {
   const int64_t ntiles = (n + kQbTile - 1) / kQbTile;
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, 8 * device_cu_count()));
-  const int lin = linear ? 1 : 0;
-  if (a_dtype == kF32)
-    hipLaunchKernelGGL(quantize_blockwise_kernel<kF32>, dim3(grid), dim3(256), 0, st, A, n, log2bs,
-                       code, lin, q, absmax);
-  else if (a_dtype == kF16)
-    hipLaunchKernelGGL(quantize_blockwise_kernel<kF16>, dim3(grid), dim3(256), 0, st, A, n, log2bs,
-                       code, lin, q, absmax);
-  else
-    hipLaunchKernelGGL(quantize_blockwise_kernel<kBF16>, dim3(grid), dim3(256), 0, st, A, n, log2bs,
-                       code, lin, q, absmax);
+  if (a_dtype == kF32) launch_qb_t<kF32>(ntiles, A, n, log2bs, code, linear, q, absmax, st);
+  else if (a_dtype == kF16) launch_qb_t<kF16>(ntiles, A, n, log2bs, code, linear, q, absmax, st);
+  else launch_qb_t<kBF16>(ntiles, A, n, log2bs, code, linear, q, absmax, st);
   return hipGetLastError();
 }
 

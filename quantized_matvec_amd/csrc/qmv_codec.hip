@@ -296,7 +296,11 @@ static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, co
   constexpr int E = 16;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, 8 * device_cu_count()));
+  // one resident generation of workgroups, each striding over the tiles
+  static const int occ = resident_wgs_per_cu(
+      reinterpret_cast<const void *>(&quantize_4bit_kernel<DT, QT, E>), 256);
+  const int64_t slots = (int64_t)device_cu_count() * occ;
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, slots));
   hipLaunchKernelGGL((quantize_4bit_kernel<DT, QT, E>), dim3(grid), dim3(256), 0, st, W, numel,
                      log2bs, qa, packed, absmax);
   return hipGetLastError();

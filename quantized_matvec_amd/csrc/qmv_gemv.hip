@@ -613,6 +613,13 @@ int device_cu_count() {
   return cached[dev];
 }
 
+int resident_wgs_per_cu(const void *kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
 template <int M, int XDT>
 static hipError_t launch_lut_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                                const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,

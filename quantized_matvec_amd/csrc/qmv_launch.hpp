@@ -48,6 +48,11 @@ hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Workgroups of `threads` threads of `kernel` resident on one compute unit at
+// once (at least 1).  A grid-stride kernel launched with this many per unit
+// runs in one generation, with no partly filled second one.
+int resident_wgs_per_cu(const void *kernel, int threads);
+
 // True when gemm_4bit takes its narrow kernel: M <= 16 rows, blocks of 64 or
 // more, K a multiple of 64 (below 2^23).
 inline bool gemm_narrow_eligible(int64_t M, int64_t K, int log2bs) {
