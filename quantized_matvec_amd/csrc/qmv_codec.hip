@@ -649,6 +649,25 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
   const int wave = tid >> 6;
   if (tid < 255) mid[tid] = ((double)code2.v[tid] + (double)code2.v[tid + 1]) * 0.5;  // exact
   if (code2_out && blockIdx.x == 0) code2_out[tid] = code2.v[tid];
+
+  const int G = (1 << log2bs2) / E;  // threads per group: 2 .. 256
+  const int64_t tile = (int64_t)256 * E;
+  const int64_t ntiles = (n + tile - 1) / tile;
+  // a tile's scales through a range-limited buffer: no branch per load.  The
+  // first tile is loaded before the offset is formed, so the two memory round
+  // trips overlap.
+  float a[E];
+  auto load_tile = [&](int64_t tt) {
+    const int64_t rem = n - tt * tile;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(absmax + tt * tile, (uint32_t)((rem < tile ? rem : tile) * sizeof(float)));
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, (uint32_t)((tid * E + e) * 4), 0, 0));
+  };
+  if (blockIdx.x < ntiles) load_tile(blockIdx.x);
+
   float off;
   if (nl > 1 && nl <= kTopFused) {
     off = fused_offset(levels, nl, stats, n, red);
@@ -658,21 +677,9 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
   }
   __syncthreads();
 
-  const int G = (1 << log2bs2) / E;  // threads per group: 2 .. 256
-  const int64_t tile = (int64_t)256 * E;
-  const int64_t ntiles = (n + tile - 1) / tile;
-
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t i0 = t * tile + (int64_t)tid * E;
-    // the tile's scales through a range-limited buffer: no branch per load
-    const int64_t rem = n - t * tile;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(absmax + t * tile, (uint32_t)((rem < tile ? rem : tile) * sizeof(float)));
-    float a[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      a[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rs, (uint32_t)((tid * E + e) * 4), 0, 0));
+    if (t != (int64_t)blockIdx.x) load_tile(t);
     float c[E];
     float m = 0.f;
 #pragma unroll
