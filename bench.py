@@ -12,7 +12,9 @@ bandwidth: algorithmic bytes per launch / average launch duration, timed with
 HIP events on the launch stream while rotating over distinct weight copies
 (> 512 MB, twice the 256 MB Infinity Cache) so the bytes come from HBM.
 Each kernel is also timed alone, including gemm_4bit_backward (dX = dY @
-W_hat with a bf16 dY [512, 14336]), which is not part of the step.
+W_hat with a bf16 dY [512, 14336]) and the 8-bit blockwise codec on the same
+bf16 weight (blocksize 4096; linear and dynamic-tree tables), which are not
+part of the step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -33,6 +35,7 @@ METRIC = "gemv_4bit achieved HBM GB/s (NF4, 14336x4096, M=1) + codec GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 N, K, BS, BS2, M_GEMV, M_GEMM = 14336, 4096, 64, 256, 1, 512
+BS8 = 4096                     # 8-bit blockwise codec block size
 ROTATE_BYTES = 640 << 20       # > 2 x 256 MB Infinity Cache
 
 
@@ -47,6 +50,10 @@ def algorithmic_bytes():
         "dequantize_4bit": packed + dq_state + 2 * numel,
         "gemv_4bit": packed + dq_state + 2 * K * M_GEMV + 2 * N * M_GEMV,
         "gemm_4bit": packed + dq_state + 2 * K * M_GEMM + 2 * N * M_GEMM,
+        # 8-bit blockwise codec: bf16 in / out, one code byte and fp32 scales
+        "quantize_blockwise": 2 * numel + numel + 4 * (numel // BS8),
+        "quantize_blockwise_dynamic": 2 * numel + numel + 4 * (numel // BS8),
+        "dequantize_blockwise": numel + 4 * (numel // BS8) + 2 * numel,
     }
 
 
@@ -268,11 +275,29 @@ def main():
             L.qmv_gemm_4bit_backward(dY_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0,
                                      dX_ptr, 2, s_h)
 
+        # the 8-bit blockwise codec on the same bf16 weights (blocksize 4096),
+        # with the default linear table and with the dynamic-tree table
+        q8 = [torch.empty(N * K, dtype=torch.uint8, device=dev) for _ in range(n_w)]
+        a8 = [torch.empty(N * K // BS8, dtype=torch.float32, device=dev) for _ in range(n_w)]
+        tree = (ctypes.c_float * 256)(*qmv.dynamic_tree_code())
+        tree_p = ctypes.cast(tree, ctypes.c_void_p)
+
+        def run_q8(i, code=None):
+            L.qmv_quantize_blockwise(Ws[i % n_w].data_ptr(), 2, N * K, BS8, code, q8[i % n_w].data_ptr(),
+                                     a8[i % n_w].data_ptr(), s_h)
+
+        def run_dq8(i):
+            L.qmv_dequantize_blockwise(q8[i % n_w].data_ptr(), a8[i % n_w].data_ptr(), N * K, BS8, None,
+                                       w_ptr[i % n_w], 2, s_h)
+
         for name, fn, iters in (("gemv_4bit", run_gemv, kiters), ("gemm_4bit", run_gemm, kiters // 4),
                                 ("gemm_4bit_backward", run_bwd, kiters // 8),
                                 ("dequantize_4bit", run_deq, kiters // 4),
                                 ("quantize_4bit", run_quant, kiters // 4),
-                                ("double_quant", run_dq, kiters // 4)):
+                                ("double_quant", run_dq, kiters // 4),
+                                ("quantize_blockwise", run_q8, kiters // 4),
+                                ("quantize_blockwise_dynamic", lambda i: run_q8(i, tree_p), kiters // 4),
+                                ("dequantize_blockwise", run_dq8, kiters // 4)):
             for i in range(5):
                 fn(i)
             kern[name] = timed_loop(fn, iters, stream, torch)
@@ -280,13 +305,13 @@ def main():
     rep = {}
     for name, us in kern.items():
         e = {"us_per_launch": round(us, 3)}
-        if name == "gemv_4bit" or name == "dequantize_4bit":
-            b = ab[name]
-            e.update(bytes=b, gbs=round(b / us / 1e3, 1), hbm_frac=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
-        elif name in ("gemm_4bit", "gemm_4bit_backward"):
+        if name in ("gemm_4bit", "gemm_4bit_backward"):
             fl = 2.0 * M_GEMM * N * K
             e.update(flops=fl, tflops=round(fl / us / 1e6, 2),
                      mfma_frac=round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4))
+        elif name in ab:
+            b = ab[name]
+            e.update(bytes=b, gbs=round(b / us / 1e3, 1), hbm_frac=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
         rep[name] = e
     q_us = kern["quantize_4bit"] + kern["double_quant"]
     b = ab["quantize_4bit+double_quant"]
