@@ -241,10 +241,12 @@ def main():
         w_ptr = [w.data_ptr() for w in wout]
 
         def run_gemv(i):
-            L.qmv_gemv_4bit(x_ptr, 2, M_GEMV, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, y_ptr, 2, s_h)
+            L.qmv_gemv_4bit(x_ptr, 2, M_GEMV, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, y_ptr, 2, None,
+                            s_h)
 
         def run_gemm(i):
-            L.qmv_gemm_4bit(A_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, C_ptr, 2, s_h)
+            L.qmv_gemm_4bit(A_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, C_ptr, 2, None,
+                            s_h)
 
         def run_deq(i):
             L.qmv_dequantize_4bit(p_ptr[i % n_p], scs[i % n_p], N * K, BS, 0, w_ptr[i % n_w], 2, s_h)

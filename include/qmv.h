@@ -134,23 +134,37 @@ int qmv_dequantize_4bit(const uint8_t *packed, const qmv_absmax *scales, int64_t
  *   y[m, n] = sum_k x[m, k] * W_hat[n, k], fp32 accumulation.
  *   x  [M, K] device row-major, x_dtype;  y [M, N] device row-major, y_dtype
  *   W_hat is [N, K]: packed [N * K / 2], scales for N * K / blocksize blocks.
+ *   bias  NULL, or [N] device in y_dtype ("mps-bitsandbytes 0.4.7",
+ *         "Functional API": matmul_nf4's bias argument): y[m, n] = the fp32
+ *         sum + fp32(bias[n]), one fp32 addition, then one rounding to y_dtype.
+ *         Aligned to its element size (QMV_ERR_ALIGNMENT).
+ * x_dtype fp32 computes in fp32 (fp32 weights and products); bf16 / fp16 x
+ * multiply the weights rounded to x's type ("Feat/mps gemm 4bit bf16",
+ * "Performance": gemv over fp16 / bf16 / fp32).
  * Requires K % blocksize == 0 and K % 32 == 0 ("unsupported blocksize" and
  * "K % 32 != 0" are the guards the PR page lists), else QMV_ERR_UNSUPPORTED.
  */
 int qmv_gemv_4bit(const void *x, qmv_dtype x_dtype, int32_t M, int64_t N, int64_t K,
                   const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
-                  qmv_quant_type quant_type, void *y, qmv_dtype y_dtype, void *stream);
+                  qmv_quant_type quant_type, void *y, qmv_dtype y_dtype, const void *bias,
+                  void *stream);
 
 /*
- * gemm_4bit: general M ("What runs natively now": gemm_4bit).  The weight is
- * dequantized tile by tile into LDS as bf16 and multiplied with bf16 matrix
- * cores, fp32 accumulation.
- *   A [M, K] device row-major bf16;  C [M, N] device row-major, c_dtype
- * Requires a_dtype == QMV_BF16, K % blocksize == 0 and K % 32 == 0.
+ * gemm_4bit: general M ("What runs natively now": gemm_4bit).
+ *   A [M, K] device row-major, a_dtype;  C [M, N] device row-major, c_dtype
+ *   bias  NULL or [N] in c_dtype, as for gemv_4bit ("Functional API":
+ *         matmul_nf4(..., bias)).
+ * a_dtype bf16 / fp16: the weight is dequantized tile by tile into LDS exactly
+ * as dequantize_4bit returns it in a_dtype and multiplied on the matrix cores
+ * in that type (v_mfma_f32_32x32x16_bf16 / _f16), fp32 accumulation.
+ * a_dtype fp32: fp32 weights, products and sums on the vector units, 8 rows
+ * per pass (slow for large M).
+ * Requires K % blocksize == 0 and K % 32 == 0.
  */
 int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_t K,
                   const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
-                  qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, void *stream);
+                  qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, const void *bias,
+                  void *stream);
 
 /*
  * quantize_blockwise / dequantize_blockwise: the general 8-bit blockwise codec
@@ -181,11 +195,12 @@ int qmv_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, i
  * gemm 4bit bf16", table "What runs natively now": gemm_4bit_backward, the
  * fused form of grad_output @ dequantize_4bit(B)).
  *   dX[m, k] = sum_n dY[m, n] * W_hat[n, k], fp32 accumulation.
- *   dY [M, N] device row-major bf16;  dX [M, K] device row-major, dx_dtype
+ *   dY [M, N] device row-major bf16 or fp16;  dX [M, K] device row-major, dx_dtype
  *   W_hat [N, K] as for gemm_4bit (the same packed codes and scales).
  * The weight is dequantized tile by tile into LDS exactly as by
- * dequantize_4bit to bf16 and multiplied with bf16 matrix cores.
- * Requires dy_dtype == QMV_BF16, N % 32 == 0, K % blocksize == 0 and
+ * dequantize_4bit to dY's type and multiplied on the matrix cores in that
+ * type.  No bias: the backward has no epilogue.
+ * Requires dy_dtype bf16 or fp16, N % 32 == 0, K % blocksize == 0 and
  * K % 32 == 0, else QMV_ERR_UNSUPPORTED.  Buffers are the caller's; dX is
  * fully overwritten.
  */

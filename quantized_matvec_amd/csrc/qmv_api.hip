@@ -232,9 +232,16 @@ int qmv_dequantize_4bit(const uint8_t *packed, const qmv_absmax *scales, int64_t
                                               quant_type, out, out_dtype, (hipStream_t)stream));
 }
 
+// bias: NULL, or [N] elements of the output type at their natural alignment.
+static bool bias_aligned(const void *bias, qmv_dtype out_dtype) {
+  const uintptr_t a = out_dtype == QMV_F32 ? 4 : 2;
+  return bias == nullptr || (reinterpret_cast<uintptr_t>(bias) % a) == 0;
+}
+
 int qmv_gemv_4bit(const void *x, qmv_dtype x_dtype, int32_t M, int64_t N, int64_t K,
                   const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
-                  qmv_quant_type quant_type, void *y, qmv_dtype y_dtype, void *stream) {
+                  qmv_quant_type quant_type, void *y, qmv_dtype y_dtype, const void *bias,
+                  void *stream) {
   if (!x || !packed || !y || !valid_dtype(x_dtype) || !valid_dtype(y_dtype))
     return QMV_ERR_INVALID_ARG;
   int rc = check_matmul(M, N, K, blocksize, quant_type);
@@ -244,27 +251,29 @@ int qmv_gemv_4bit(const void *x, qmv_dtype x_dtype, int32_t M, int64_t N, int64_
   bool dq;
   rc = check_scales(scales, &sc, &dq);
   if (rc != QMV_OK) return rc;
-  if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return QMV_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !bias_aligned(bias, y_dtype))
+    return QMV_ERR_ALIGNMENT;
   return launch_status(launch_gemv_4bit(x, x_dtype, M, N, K, packed, sc, dq, log2_exact(blocksize),
-                                        quant_type, y, y_dtype, (hipStream_t)stream));
+                                        quant_type, y, y_dtype, bias, (hipStream_t)stream));
 }
 
 int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_t K,
                   const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
-                  qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, void *stream) {
+                  qmv_quant_type quant_type, void *C, qmv_dtype c_dtype, const void *bias,
+                  void *stream) {
   if (!A || !packed || !C || !valid_dtype(a_dtype) || !valid_dtype(c_dtype))
     return QMV_ERR_INVALID_ARG;
   int rc = check_matmul(M, N, K, blocksize, quant_type);
   if (rc != QMV_OK) return rc;
-  if (a_dtype != QMV_BF16) return QMV_ERR_UNSUPPORTED;
   if ((M + 127) / 128 > 65535) return QMV_ERR_UNSUPPORTED;
   Scales sc;
   bool dq;
   rc = check_scales(scales, &sc, &dq);
   if (rc != QMV_OK) return rc;
-  if (!aligned16(A) || !aligned16(packed) || !aligned16(C)) return QMV_ERR_ALIGNMENT;
-  return launch_status(launch_gemm_4bit(A, M, N, K, packed, sc, dq, log2_exact(blocksize),
-                                        quant_type, C, c_dtype, (hipStream_t)stream));
+  if (!aligned16(A) || !aligned16(packed) || !aligned16(C) || !bias_aligned(bias, c_dtype))
+    return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_gemm_4bit(A, a_dtype, M, N, K, packed, sc, dq, log2_exact(blocksize),
+                                        quant_type, C, c_dtype, bias, (hipStream_t)stream));
 }
 
 int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_t N, int64_t K,
@@ -274,14 +283,14 @@ int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_
     return QMV_ERR_INVALID_ARG;
   int rc = check_matmul(M, N, K, blocksize, quant_type);
   if (rc != QMV_OK) return rc;
-  if (dy_dtype != QMV_BF16 || N % 32 != 0) return QMV_ERR_UNSUPPORTED;
+  if (dy_dtype == QMV_F32 || N % 32 != 0) return QMV_ERR_UNSUPPORTED;
   if ((M + 127) / 128 > 65535) return QMV_ERR_UNSUPPORTED;
   Scales sc;
   bool dq;
   rc = check_scales(scales, &sc, &dq);
   if (rc != QMV_OK) return rc;
   if (!aligned16(dY) || !aligned16(packed) || !aligned16(dX)) return QMV_ERR_ALIGNMENT;
-  return launch_status(launch_gemm_4bit_backward(dY, M, N, K, packed, sc, dq, log2_exact(blocksize),
+  return launch_status(launch_gemm_4bit_backward(dY, dy_dtype, M, N, K, packed, sc, dq, log2_exact(blocksize),
                                                  quant_type, dX, dx_dtype, (hipStream_t)stream));
 }
 

@@ -24,6 +24,28 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+
+// One 32 x 32 x 16 matrix-core step on 16-bit inputs of type ADT (bf16 or
+// fp16; operands carried as raw 16-bit patterns, 8 k-values per lane), fp32
+// accumulation: v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x16_f16.
+template <int ADT>
+__device__ __forceinline__ f32x16_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const f32x16_t &c) {
+  if constexpr (ADT == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Output element with the optional bias: fp32 accumulator + fp32(bias[n]),
+// one fp32 addition, then one rounding to the output type.
+template <int CDT>
+__device__ __forceinline__ void store_out(typename Storage<CDT>::type *C, int64_t idx, float v,
+                                          const typename Storage<CDT>::type *bias, int64_t n) {
+  if (bias) v = v + load_elem<CDT>(bias, n);
+  store_elem<CDT>(C, idx, v);
+}
 
 // Tile: BM (M, 128 or 256) x BN (N, 128 or 64) x 64 (K) for NT = 2 BM
 // threads; the waves form (BM / 64) x WN, each computing 64 x BN / WN as
@@ -41,12 +63,13 @@ struct Table16f {
   float v[16];
 };
 
-template <int CDT, bool DQ, int BM, int BN>
+template <int ADT, int CDT, bool DQ, int BM, int BN>
 __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(const uint16_t *__restrict__ A, int64_t M,
                                                            int64_t N, int64_t K,
                                                            const uint8_t *__restrict__ packed,
                                                            Scales sc, int log2bs, Table16f table,
-                                                           void *__restrict__ Cv) {
+                                                           void *__restrict__ Cv,
+                                                           const void *__restrict__ biasv) {
   constexpr int NT = 2 * BM;                // threads
   constexpr int kStage = (BM + BN) * kLd;   // bf16 elements per stage
   constexpr int WN = NT / 64 / (BM / 64);   // waves along N (2)
@@ -57,6 +80,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
   using CT = typename Storage<CDT>::type;
   using PW = typename std::conditional<BPT == 32, uint4, uint2>::type;  // packed bytes per thread
   CT *C = static_cast<CT *>(Cv);
+  const CT *bias = static_cast<const CT *>(biasv);
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
   __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
   __shared__ float code2[256];
@@ -122,9 +146,9 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
 #pragma unroll
     for (int bb = 0; bb < BPT / 2; ++bb) {
       const float2 t = lut2[(pw[bb >> 2] >> (8 * (bb & 3))) & 0xffu];
-      // dequantized weights: fp32(T * a_hat) rounded to bf16 (nearest even)
-      const f32x2_t v = {materialize(t.x * a), materialize(t.y * a)};
-      o[bb] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+      // dequantized weights: fp32(T * a_hat) rounded to the input's 16-bit
+      // type (nearest even), as dequantize_4bit returns them
+      o[bb] = cvt_pair<ADT>(t.x * a, t.y * a);
     }
     uint4 *bd = reinterpret_cast<uint4 *>(Bs + br * kLd + BPT * bq);
 #pragma unroll
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma16<ADT>(af[i], bfr[j], acc[i][j]);
     }
   };
 
@@ -203,7 +227,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) store_elem<CDT>(C, row * N + col, acc[i][j][r]);
+        if (row < M) store_out<CDT>(C, row * N + col, acc[i][j][r], bias, col);
       }
     }
 }
@@ -227,12 +251,13 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
 // exactly as in the tile kernel (fp32(T * a_hat) rounded to bf16).  The next
 // step's loads are issued before the current step is computed.
 // ---------------------------------------------------------------------------
-template <int CDT, bool DQ, int MT, int KW>
+template <int ADT, int CDT, bool DQ, int MT, int KW>
 __global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
     const uint16_t *__restrict__ A, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    Scales sc, int log2bs, Table16f table, void *__restrict__ Cv) {
+    Scales sc, int log2bs, Table16f table, void *__restrict__ Cv, const void *__restrict__ biasv) {
   using CT = typename Storage<CDT>::type;
   CT *C = static_cast<CT *>(Cv);
+  const CT *bias = static_cast<const CT *>(biasv);
   __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
   __shared__ float code2[256];
   __shared__ float red[(KW - 1) * MT * 16 * 64];
@@ -308,15 +333,13 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
       uint32_t bw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // dequantized weights: fp32(T * a_hat) rounded to bf16 (nearest even)
-        const f32x2_t v = {materialize(tv[4 * j + q].x * a), materialize(tv[4 * j + q].y * a)};
-        bw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        // dequantized weights: fp32(T * a_hat) rounded to the input's type
+        bw[q] = cvt_pair<ADT>(tv[4 * j + q].x * a, tv[4 * j + q].y * a);
       }
       const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, r.a[t][j]), bop,
-                                                         acc[t], 0, 0, 0);
+        acc[t] = mfma16<ADT>(__builtin_bit_cast(bf16x8_t, r.a[t][j]), bop, acc[t]);
     }
   };
 
@@ -352,7 +375,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
         for (int w = 1; w < KW; ++w) v += red[(((w - 1) * MT + t) * 16 + i) * 64 + lane];
         // accumulator layout: column = lane % 32, row = 8 (i / 4) + 4 (lane / 32) + i % 4
         const int64_t m = 32 * t + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (m < M) store_elem<CDT>(C, m * N + n, v);
+        if (m < M) store_out<CDT>(C, m * N + n, v, bias, n);
       }
   }
 }
@@ -406,10 +429,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint4 *dst
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, 0, 0, 0);
 }
 
-template <int CDT, bool DQ, int MP, int NB, int KW>
+template <int ADT, int CDT, bool DQ, int MP, int NB, int KW>
 __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
     const uint16_t *__restrict__ A, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
-    Scales sc, int log2bs, Table16f table, void *__restrict__ Cv) {
+    Scales sc, int log2bs, Table16f table, void *__restrict__ Cv, const void *__restrict__ biasv) {
   constexpr int WCH = 128;              // weight chunks per group (32 rows x 64 bytes)
   constexpr int ACH = 16 * MP;          // activation chunks per group (MP rows x 128 k-values)
   constexpr int WND = WCH / 64, AND = ACH / 64;  // LDS-direct loads per group
@@ -420,7 +443,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
                 "narrow gemm shape");
   using CT = typename Storage<CDT>::type;
   CT *C = static_cast<CT *>(Cv);
-  __shared__ uint32_t lut[256];  // packed byte -> (bf16 T[byte >> 4], bf16 T[byte & 15])
+  __shared__ uint32_t lut[256];  // packed byte -> (T[byte >> 4], T[byte & 15]) as the input type
   __shared__ float code2[256];
   __shared__ float red[(KW - 1) * RR * 64];
   // one array per ring slot, so that the compiler can tell an LDS-direct load
@@ -514,7 +537,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
   // prologue: groups 0 .. NB - 2 in flight while the tables are built
   static_for<NB - 1>([&](auto U) { issue(decltype(U)::value, U); });
   if (tid < 256) {
-    lut[tid] = f32_to_bf16_rne(table.v[tid >> 4]) | (f32_to_bf16_rne(table.v[tid & 15]) << 16);
+    lut[tid] = f32_to_bits16<ADT>(table.v[tid >> 4]) | (f32_to_bits16<ADT>(table.v[tid & 15]) << 16);
     if constexpr (DQ) code2[tid] = c2v;
   }
   if (lane < NB) {
@@ -544,9 +567,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
           uint32_t bw[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) bw[q] = lut[(pw[j] >> (8 * q)) & 0xffu];
-          tile = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, sl[ard[t][j]]),
-              __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3])), tile, 0, 0, 0);
+          tile = mfma16<ADT>(__builtin_bit_cast(bf16x8_t, sl[ard[t][j]]),
+                             __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3])), tile);
         }
         const float a = DQ ? code2[sr[u].q[t]] * sr[u].s[t] + offset : sr[u].s[t];  // block scale
 #pragma unroll
@@ -585,14 +607,15 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
       for (int w = 1; w < KW; ++w) v += red[((w - 1) * RR + e) * 64 + lane];
       // accumulator layout: column = lane % 32, row = 8 (e / 4) + 4 (lane / 32) + e % 4
       const int64_t m = 8 * (e >> 2) + 4 * kh + (e & 3);
-      if (m < M) store_elem<CDT>(C, m * N + n, v);
+      if (m < M) store_out<CDT>(C, m * N + n, v, static_cast<const CT *>(biasv), n);
     }
   }
 }
 
-hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                            const Scales &sc, bool dq, int log2bs, int qt, void *C, int c_dtype,
-                            hipStream_t st) {
+template <int ADT>
+static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                int qt, void *C, int c_dtype, const void *bias, hipStream_t st) {
   const uint16_t *a = static_cast<const uint16_t *>(A);
   Table16f table;
   const uint32_t *bits = table_bits(qt);
@@ -600,8 +623,8 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
   if (gemm_narrow_eligible(M, K, log2bs)) {  // narrow M
     const dim3 sgrid((unsigned)((N + 31) / 32));
 #define QMV_N(CDT, DQV, MPV, NBV, KWV)                                                          \
-  hipLaunchKernelGGL((gemm_4bit_narrow_kernel<CDT, DQV, MPV, NBV, KWV>), sgrid, dim3(64 * KWV), 0, \
-                     st, a, M, N, K, packed, sc, log2bs, table, C)
+  hipLaunchKernelGGL((gemm_4bit_narrow_kernel<ADT, CDT, DQV, MPV, NBV, KWV>), sgrid, dim3(64 * KWV), \
+                     0, st, a, M, N, K, packed, sc, log2bs, table, C, bias)
 #define QMV_NM(CDT, DQV)                        \
   if (M <= 8) { QMV_N(CDT, DQV, 8, 2, 4); }     \
   else { QMV_N(CDT, DQV, 16, 2, 4); }
@@ -618,8 +641,8 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
   if (M <= 64 && K % 64 == 0 && K < (1 << 23)) {  // skinny M: N / 32 workgroups of 8 waves splitting K
     const dim3 sgrid((unsigned)((N + 31) / 32));
 #define QMV_S(CDT, DQV, MTV)                                                                   \
-  hipLaunchKernelGGL((gemm_4bit_skinny_kernel<CDT, DQV, MTV, 8>), sgrid, dim3(512), 0, st, a, M, \
-                     N, K, packed, sc, log2bs, table, C)
+  hipLaunchKernelGGL((gemm_4bit_skinny_kernel<ADT, CDT, DQV, MTV, 8>), sgrid, dim3(512), 0, st, a, \
+                     M, N, K, packed, sc, log2bs, table, C, bias)
 #define QMV_SM(CDT, DQV) \
   if (M <= 32) { QMV_S(CDT, DQV, 1); } else { QMV_S(CDT, DQV, 2); }
 #define QMV_SD(CDT) \
@@ -640,8 +663,8 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
   const dim3 grid((unsigned)(shape ? nt128 : (N + 63) / 64),
                   (unsigned)(shape == 2 ? (M + 255) / 256 : (M + 127) / 128));
 #define QMV_M(CDT, DQV, BMV, BNV)                                                                    \
-  hipLaunchKernelGGL((gemm_4bit_kernel<CDT, DQV, BMV, BNV>), grid, dim3(2 * BMV), 0, st, a, M, N, K, \
-                     packed, sc, log2bs, table, C)
+  hipLaunchKernelGGL((gemm_4bit_kernel<ADT, CDT, DQV, BMV, BNV>), grid, dim3(2 * BMV), 0, st, a, M, N, \
+                     K, packed, sc, log2bs, table, C, bias)
 #define QMV_MB(CDT, DQV)                                     \
   if (shape == 2) { QMV_M(CDT, DQV, 256, 128); }             \
   else if (shape == 1) { QMV_M(CDT, DQV, 128, 128); }        \
@@ -655,6 +678,27 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
 #undef QMV_MB
 #undef QMV_M
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, int64_t K,
+                            const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
+                            void *C, int c_dtype, const void *bias, hipStream_t st) {
+  if (a_dtype == kF32) {
+    // fp32 activations: the fp32 kernel of gemv_4bit (fp32 weights, fp32
+    // products and sums) over slices of 8 rows
+    const size_t csz = c_dtype == kF32 ? 4 : 2;
+    for (int64_t m0 = 0; m0 < M; m0 += 8) {
+      const int rows = (int)std::min<int64_t>(8, M - m0);
+      const hipError_t e = launch_gemv_4bit(static_cast<const float *>(A) + m0 * K, kF32, rows, N, K,
+                                            packed, sc, dq, log2bs, qt,
+                                            static_cast<char *>(C) + (size_t)(m0 * N) * csz, c_dtype,
+                                            bias, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (a_dtype == kF16) return launch_gemm_t<kF16>(A, M, N, K, packed, sc, dq, log2bs, qt, C, c_dtype, bias, st);
+  return launch_gemm_t<kBF16>(A, M, N, K, packed, sc, dq, log2bs, qt, C, c_dtype, bias, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -673,7 +717,7 @@ hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, cons
 // rounded to bf16, so the matrix cores see the dequantize_4bit weights.
 // Requires N % 32 == 0 (a step past N is half zero) and K % 32 == 0.
 // ---------------------------------------------------------------------------
-template <int CDT, bool DQ, int BN, int G>
+template <int ADT, int CDT, bool DQ, int BN, int G>
 __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint16_t *__restrict__ dY,
                                                                       int64_t M, int64_t N, int64_t K,
                                                                       const uint8_t *__restrict__ packed,
@@ -755,8 +799,7 @@ __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float2 tv = lut2[(rb_[SL][r] >> (8 * i)) & 0xffu];
-        const f32x2_t v = {materialize(tv.x * a), materialize(tv.y * a)};
-        w[r][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        w[r][i] = cvt_pair<ADT>(tv.x * a, tv.y * a);
       }
     }
     // column c = 8 o + 2 i (+1): its RN values, rows in order, in one store
@@ -817,7 +860,7 @@ __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma16<ADT>(af[i], bfr[j], acc[i][j]);
     }
   };
 
@@ -877,9 +920,10 @@ __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint
     }
 }
 
-hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64_t K,
-                                     const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
-                                     int qt, void *dX, int dx_dtype, hipStream_t st) {
+template <int ADT>
+static hipError_t launch_backward_t(const void *dY, int64_t M, int64_t N, int64_t K,
+                                    const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                    int qt, void *dX, int dx_dtype, hipStream_t st) {
   const uint16_t *g = static_cast<const uint16_t *>(dY);
   Table16f table;
   const uint32_t *bits = table_bits(qt);
@@ -888,7 +932,7 @@ hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64
   const bool wide = ((K + 127) / 128) * mt >= (int64_t)device_cu_count();
   const dim3 grid((unsigned)(wide ? (K + 127) / 128 : (K + 63) / 64), (unsigned)mt);
 #define QMV_B(CDT, DQV, BNV)                                                                    \
-  hipLaunchKernelGGL((gemm_4bit_dx_kernel<CDT, DQV, BNV, 2>), grid, dim3(512), 0, st, g, M, N, K, \
+  hipLaunchKernelGGL((gemm_4bit_dx_kernel<ADT, CDT, DQV, BNV, 2>), grid, dim3(512), 0, st, g, M, N, K, \
                      packed, sc, log2bs, table, dX)
 #define QMV_BB(CDT, DQV) \
   if (wide) { QMV_B(CDT, DQV, 128); } else { QMV_B(CDT, DQV, 64); }
@@ -901,6 +945,13 @@ hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64
 #undef QMV_BB
 #undef QMV_B
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_4bit_backward(const void *dY, int dy_dtype, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                     int qt, void *dX, int dx_dtype, hipStream_t st) {
+  if (dy_dtype == kF16) return launch_backward_t<kF16>(dY, M, N, K, packed, sc, dq, log2bs, qt, dX, dx_dtype, st);
+  return launch_backward_t<kBF16>(dY, M, N, K, packed, sc, dq, log2bs, qt, dX, dx_dtype, st);
 }
 
 }  // namespace qmv

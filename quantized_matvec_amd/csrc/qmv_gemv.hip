@@ -77,7 +77,15 @@ __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
                                   acc, false);
 }
 
-__device__ __forceinline__ void store_y(void *y, int ydt, int64_t i, float v) {
+// y[i] = v (+ bias[n], in the output type, added in fp32), rounded once to
+// the output type.
+__device__ __forceinline__ void store_y(void *y, int ydt, int64_t i, float v, const void *bias,
+                                        int64_t n) {
+  if (bias) {
+    if (ydt == kF32) v = v + static_cast<const float *>(bias)[n];
+    else if (ydt == kBF16) v = v + bits16_to_f32<kBF16>(static_cast<const uint16_t *>(bias)[n]);
+    else v = v + bits16_to_f32<kF16>(static_cast<const uint16_t *>(bias)[n]);
+  }
   if (ydt == kF32) static_cast<float *>(y)[i] = v;
   else if (ydt == kBF16) static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_bf16_rne(v);
   else static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_f16_rne(v);
@@ -118,7 +126,7 @@ template <int M, int XDT, bool DQ>
 __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSimd) void gemv_4bit_lut_kernel(
     const uint16_t *__restrict__ x, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
-    int rows_rem) {
+    int rows_rem, const void *__restrict__ bias) {
   constexpr int RG = LutShape<M>::RG;
   constexpr int kGemvThreads = LutShape<M>::kThreads;
   constexpr bool PX = LutShape<M>::kPrefetchX;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSim
         for (int m = 0; m < M; ++m) {
           const float v = wave_sum(acc[r][m]);
           acc[r][m] = 0.f;
-          if (lane == r * M + m && row < r_end) store_y(y, ydt, m * N + row, v);
+          if (lane == r * M + m && row < r_end) store_y(y, ydt, m * N + row, v, bias, row);
         }
       }
     }
@@ -295,7 +303,7 @@ template <int XDT, bool DQ, int XC, int RPS>  // XC: x chunks staged per thread 
 __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
     const uint16_t *__restrict__ x, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
-    int rows_rem) {
+    int rows_rem, const void *__restrict__ bias) {
   constexpr bool XLDS = XC > 0;
   constexpr int D = m1_depth<RPS>();  // steps in flight
   // one LDS block with the code-pair table at address 0, so a lookup address
@@ -454,7 +462,7 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
       for (int r = 0; r < RPS; ++r) {
         if (g * RPS + r < nrows) {
           const float v = wave_sum(acc[r]);
-          if (lane == r) store_y(y, ydt, r_begin + g * RPS + r, v);
+          if (lane == r) store_y(y, ydt, r_begin + g * RPS + r, v, bias, r_begin + g * RPS + r);
         }
         acc[r] = 0.f;
       }
@@ -500,9 +508,11 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
 template <int M, int XDT, int YDT, bool DQ, int QT>
 __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restrict__ xv, int64_t N,
                                                         int64_t K, const uint8_t *__restrict__ packed,
-                                                        Scales sc, int log2bs, void *__restrict__ yv) {
+                                                        Scales sc, int log2bs, void *__restrict__ yv,
+                                                        const void *__restrict__ biasv) {
   using XT = typename Storage<XDT>::type;
   using YT = typename Storage<YDT>::type;
+  const YT *bias = static_cast<const YT *>(biasv);
   const XT *x = static_cast<const XT *>(xv);
   YT *y = static_cast<YT *>(yv);
   __shared__ float lut[16];
@@ -548,7 +558,11 @@ __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restr
     }
     if (lane == 0) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) store_elem<YDT>(y, m * N + n, acc[m]);
+      for (int m = 0; m < M; ++m) {
+        float v = acc[m];
+        if (bias) v = v + load_elem<YDT>(bias, n);  // one fp32 add, then one rounding
+        store_elem<YDT>(y, m * N + n, v);
+      }
     }
   }
 }
@@ -559,11 +573,11 @@ __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restr
 template <int M, int YDT>
 static hipError_t launch_f32x_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                                 const Scales &sc, bool dq, int log2bs, int qt, void *y,
-                                hipStream_t st) {
+                                const void *bias, hipStream_t st) {
   const unsigned grid = (unsigned)std::min<int64_t>((N + 3) / 4, 1 << 16);
 #define QMV_G(DQV, QTV)                                                                       \
   hipLaunchKernelGGL((gemv_4bit_f32x_kernel<M, kF32, YDT, DQV, QTV>), dim3(grid), dim3(256), 0, \
-                     st, x, N, K, packed, sc, log2bs, y)
+                     st, x, N, K, packed, sc, log2bs, y, bias)
   if (dq) {
     if (qt == kNF4) QMV_G(true, kNF4); else QMV_G(true, kFP4);
   } else {
@@ -576,12 +590,12 @@ static hipError_t launch_f32x_m(const void *x, int64_t N, int64_t K, const uint8
 template <int YDT>
 static hipError_t launch_f32x(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
                               const Scales &sc, bool dq, int log2bs, int qt, void *y,
-                              hipStream_t st) {
+                              const void *bias, hipStream_t st) {
   switch (M) {
-#define QMV_C(MV) case MV: return launch_f32x_m<MV, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
+#define QMV_C(MV) case MV: return launch_f32x_m<MV, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, bias, st);
     QMV_C(1) QMV_C(2) QMV_C(3) QMV_C(4) QMV_C(5) QMV_C(6) QMV_C(7)
 #undef QMV_C
-    default: return launch_f32x_m<8, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, st);
+    default: return launch_f32x_m<8, YDT>(x, N, K, packed, sc, dq, log2bs, qt, y, bias, st);
   }
 }
 
@@ -623,7 +637,7 @@ int resident_wgs_per_cu(const void *kernel, int threads) {
 template <int M, int XDT>
 static hipError_t launch_lut_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                                const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
-                               hipStream_t st) {
+                               const void *bias, hipStream_t st) {
   constexpr int kGemvThreads = LutShape<M>::kThreads;
   const int64_t waves_per_wg = kGemvThreads / 64;
   int64_t grid = (int64_t)device_cu_count() * LutShape<M>::kWgPerCu;
@@ -635,18 +649,18 @@ static hipError_t launch_lut_m(const void *x, int64_t N, int64_t K, const uint8_
   if (dq)
     hipLaunchKernelGGL((gemv_4bit_lut_kernel<M, XDT, true>), dim3((unsigned)grid),
                        dim3(kGemvThreads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt,
-                       rpw, rem);
+                       rpw, rem, bias);
   else
     hipLaunchKernelGGL((gemv_4bit_lut_kernel<M, XDT, false>), dim3((unsigned)grid),
                        dim3(kGemvThreads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt,
-                       rpw, rem);
+                       rpw, rem, bias);
   return hipGetLastError();
 }
 
 template <int XDT>
 static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                             const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
-                            hipStream_t st) {
+                            const void *bias, hipStream_t st) {
   const int64_t waves_per_wg = kM1Threads / 64;
   int64_t grid = (int64_t)device_cu_count();
   grid = std::min<int64_t>(grid, (N + waves_per_wg - 1) / waves_per_wg);
@@ -666,7 +680,7 @@ static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *
 #define QMV_M1(DQV, XCV, RV)                                                                   \
   hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, RV>), dim3((unsigned)grid),          \
                      dim3(kM1Threads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt, rpw, \
-                     rem)
+                     rem, bias)
 #define QMV_M1R(DQV, XCV)                                          \
   switch (rps) {                                                   \
     case 4: QMV_M1(DQV, XCV, 4); break;                            \
@@ -695,28 +709,28 @@ static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *
 template <int XDT>
 static hipError_t launch_lut(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
                              const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
-                             hipStream_t st) {
-  if (M == 1) return launch_m1<XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, st);
+                             const void *bias, hipStream_t st) {
+  if (M == 1) return launch_m1<XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
   switch (M) {
-#define QMV_C(MV) case MV: return launch_lut_m<MV, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, st);
+#define QMV_C(MV) case MV: return launch_lut_m<MV, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
     QMV_C(1) QMV_C(2) QMV_C(3) QMV_C(4) QMV_C(5) QMV_C(6) QMV_C(7)
 #undef QMV_C
-    default: return launch_lut_m<8, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, st);
+    default: return launch_lut_m<8, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
   }
 }
 
 hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_t K,
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
-                            void *y, int y_dtype, hipStream_t st) {
-  // 4 to 8 rows of bf16 activations: the MFMA kernel of gemm_4bit (the table
-  // kernel's dot products grow with M, the MFMA's do not)
-  if (x_dtype == kBF16 && M >= 4 && gemm_narrow_eligible(M, K, log2bs))
-    return launch_gemm_4bit(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
-  if (x_dtype == kBF16) return launch_lut<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
-  if (x_dtype == kF16) return launch_lut<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, st);
-  if (y_dtype == kF32) return launch_f32x<kF32>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
-  if (y_dtype == kF16) return launch_f32x<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
-  return launch_f32x<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, st);
+                            void *y, int y_dtype, const void *bias, hipStream_t st) {
+  // 4 to 8 rows of 16-bit activations: the MFMA kernel of gemm_4bit (the
+  // table kernel's dot products grow with M, the MFMA's do not)
+  if (x_dtype != kF32 && M >= 4 && gemm_narrow_eligible(M, K, log2bs))
+    return launch_gemm_4bit(x, x_dtype, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, bias, st);
+  if (x_dtype == kBF16) return launch_lut<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, bias, st);
+  if (x_dtype == kF16) return launch_lut<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, bias, st);
+  if (y_dtype == kF32) return launch_f32x<kF32>(x, M, N, K, packed, sc, dq, log2bs, qt, y, bias, st);
+  if (y_dtype == kF16) return launch_f32x<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, bias, st);
+  return launch_f32x<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, bias, st);
 }
 
 }  // namespace qmv

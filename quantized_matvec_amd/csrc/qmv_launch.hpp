@@ -41,9 +41,11 @@ hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t nblocks, 
 hipError_t launch_dequantize_4bit(const uint8_t *packed, const Scales &sc, bool dq, int64_t numel,
                                   int log2bs, int qt, void *out, int out_dtype, hipStream_t st);
 
+// bias: NULL or [N] in the output type, added to the fp32 result before the
+// one rounding to the output type.
 hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_t K,
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
-                            void *y, int y_dtype, hipStream_t st);
+                            void *y, int y_dtype, const void *bias, hipStream_t st);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
@@ -58,9 +60,10 @@ int resident_wgs_per_cu(const void *kernel, int threads);
 inline bool gemm_narrow_eligible(int64_t M, int64_t K, int log2bs) {
   return M <= 16 && log2bs >= 6 && K % 64 == 0 && K < (1 << 23);
 }
-hipError_t launch_gemm_4bit(const void *A, int64_t M, int64_t N, int64_t K, const uint8_t *packed,
-                            const Scales &sc, bool dq, int log2bs, int qt, void *C, int c_dtype,
-                            hipStream_t st);
+// a_dtype: kBF16 or kF16 (the matrix cores' input type); bias as for gemv.
+hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, int64_t K,
+                            const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
+                            void *C, int c_dtype, const void *bias, hipStream_t st);
 
 hipError_t launch_quantize_blockwise(const void *A, int a_dtype, int64_t n, int log2bs,
                                      const Code2Table &code, bool linear, uint8_t *q,
@@ -70,7 +73,7 @@ hipError_t launch_dequantize_blockwise(const uint8_t *q, const float *absmax, in
                                        const Code2Table &code, void *out, int out_dtype,
                                        hipStream_t st);
 
-hipError_t launch_gemm_4bit_backward(const void *dY, int64_t M, int64_t N, int64_t K,
+hipError_t launch_gemm_4bit_backward(const void *dY, int dy_dtype, int64_t M, int64_t N, int64_t K,
                                      const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
                                      int qt, void *dX, int dx_dtype, hipStream_t st);
 

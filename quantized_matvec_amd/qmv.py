@@ -66,9 +66,9 @@ def lib() -> ctypes.CDLL:
         "qmv_dequantize_absmax": (ctypes.c_int, [ap, i64, vp, vp]),
         "qmv_dequantize_4bit": (ctypes.c_int, [vp, ap, i64, i32, ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_gemv_4bit": (ctypes.c_int, [vp, ctypes.c_int, i32, i64, i64, vp, ap, i32,
-                                         ctypes.c_int, vp, ctypes.c_int, vp]),
+                                         ctypes.c_int, vp, ctypes.c_int, vp, vp]),
         "qmv_gemm_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
-                                         ctypes.c_int, vp, ctypes.c_int, vp]),
+                                         ctypes.c_int, vp, ctypes.c_int, vp, vp]),
         "qmv_quantize_blockwise": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp, vp]),
         "qmv_dequantize_blockwise": (ctypes.c_int, [vp, vp, i64, i32, vp, vp, ctypes.c_int, vp]),
         "qmv_gemm_4bit_backward": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
@@ -211,7 +211,7 @@ def dequantize_4bit(packed: torch.Tensor, state: QuantState, out: Optional[torch
     return out
 
 
-def _matmul(name, x, packed, state, out, out_dtype):
+def _matmul(name, x, packed, state, out, out_dtype, bias):
     if len(state.shape) != 2:
         raise ValueError("the quantized weight must be 2-D [N, K]")
     N, K = state.shape
@@ -223,24 +223,32 @@ def _matmul(name, x, packed, state, out, out_dtype):
         out = torch.empty((M, N), dtype=out_dtype or x.dtype, device=x.device)
     elif not out.is_contiguous() or out.numel() != M * N or out.data_ptr() % 16:
         raise ValueError("out must be contiguous, 16-byte aligned and hold M * N elements")
+    bias_ptr = None
+    if bias is not None:
+        bias = _dev(bias, "bias")
+        if bias.dtype != out.dtype or bias.numel() != N:
+            raise ValueError("bias must hold N elements of the output dtype")
+        bias_ptr = bias.data_ptr()
     c = state._c()
     f = getattr(lib(), "qmv_" + name)
     _check(f(x2.data_ptr(), _DT[x2.dtype], M, N, K, packed.data_ptr(), ctypes.byref(c),
-             state.blocksize, _QT[state.quant_type], out.data_ptr(), _DT[out.dtype],
+             state.blocksize, _QT[state.quant_type], out.data_ptr(), _DT[out.dtype], bias_ptr,
              _stream(x2)), name)
     return out
 
 
 def gemv_4bit(x: torch.Tensor, packed: torch.Tensor, state: QuantState,
-              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None):
-    """y [M, N] = x [M, K] @ W_hat^T for 1 <= M <= 8."""
-    return _matmul("gemv_4bit", x, packed, state, out, out_dtype)
+              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+              bias: Optional[torch.Tensor] = None):
+    """y [M, N] = x [M, K] @ W_hat^T (+ bias [N]) for 1 <= M <= 8."""
+    return _matmul("gemv_4bit", x, packed, state, out, out_dtype, bias)
 
 
 def gemm_4bit(A: torch.Tensor, packed: torch.Tensor, state: QuantState,
-              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None):
-    """C [M, N] = A [M, K] @ W_hat^T (A in bf16)."""
-    return _matmul("gemm_4bit", A, packed, state, out, out_dtype)
+              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+              bias: Optional[torch.Tensor] = None):
+    """C [M, N] = A [M, K] @ W_hat^T (+ bias [N]); A in bf16, fp16 or fp32."""
+    return _matmul("gemm_4bit", A, packed, state, out, out_dtype, bias)
 
 
 def _code8(code):
@@ -300,7 +308,7 @@ def dynamic_tree_code() -> list:
 def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState,
                        out: Optional[torch.Tensor] = None,
                        out_dtype: Optional[torch.dtype] = None):
-    """dX [M, K] = dY [M, N] @ W_hat (dY in bf16): the input gradient of y = x @ W_hat^T."""
+    """dX [M, K] = dY [M, N] @ W_hat (dY in bf16 or fp16): the input gradient of y = x @ W_hat^T."""
     if len(state.shape) != 2:
         raise ValueError("the quantized weight must be 2-D [N, K]")
     N, K = state.shape

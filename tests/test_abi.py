@@ -120,19 +120,22 @@ def test_matmul_preconditions(qmvlib):
     sc = _scales(absmax=P2)
     gv, gm = qmvlib.qmv_gemv_4bit, qmvlib.qmv_gemm_4bit
     r = ctypes.byref(sc)
-    assert gv(P, BF16, 9, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # M > 8
-    assert gv(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
-    assert gv(P, BF16, 1, 0, 64, P, r, 64, NF4, P, BF16, None) == INVALID
-    assert gv(P, BF16, 1, 64, 96, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # K % bs
-    assert gv(P, BF16, 1, 64, 48, P, r, 32, NF4, P, BF16, None) == UNSUPPORTED   # K % 32
-    assert gv(P, BF16, 1, 64, 64, P, r, 64, NF4, MIS, BF16, None) == ALIGN
-    assert gv(None, BF16, 1, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
-    assert gm(P, F32, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED    # A must be bf16
-    assert gm(P, BF16, 8, 64, 64, P, r, 100, NF4, P, BF16, None) == UNSUPPORTED
-    assert gm(P, BF16, 8, 64, 64, P, None, 64, NF4, P, BF16, None) == INVALID
-    assert gm(P, BF16, 8, 64, 64, P, r, 64, 2, P, BF16, None) == INVALID
+    assert gv(P, BF16, 9, 64, 64, P, r, 64, NF4, P, BF16, None, None) == UNSUPPORTED   # M > 8
+    assert gv(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None, None) == INVALID
+    assert gv(P, BF16, 1, 0, 64, P, r, 64, NF4, P, BF16, None, None) == INVALID
+    assert gv(P, BF16, 1, 64, 96, P, r, 64, NF4, P, BF16, None, None) == UNSUPPORTED   # K % bs
+    assert gv(P, BF16, 1, 64, 48, P, r, 32, NF4, P, BF16, None, None) == UNSUPPORTED   # K % 32
+    assert gv(P, BF16, 1, 64, 64, P, r, 64, NF4, MIS, BF16, None, None) == ALIGN
+    assert gv(None, BF16, 1, 64, 64, P, r, 64, NF4, P, BF16, None, None) == INVALID
+    assert gv(P, BF16, 1, 64, 64, P, r, 64, NF4, P, BF16, P + 1, None) == ALIGN       # bias element
+    assert gv(P, BF16, 1, 64, 64, P, r, 64, NF4, P, F32, P + 2, None) == ALIGN
+    assert gm(P, BF16, 8, 64, 64, P, r, 100, NF4, P, BF16, None, None) == UNSUPPORTED
+    assert gm(P, BF16, 8, 64, 64, P, None, 64, NF4, P, BF16, None, None) == INVALID
+    assert gm(P, BF16, 8, 64, 64, P, r, 64, 2, P, BF16, None, None) == INVALID
+    assert gm(P, 7, 8, 64, 64, P, r, 64, NF4, P, BF16, None, None) == INVALID
+    assert gm(P, F16, 8, 64, 64, P, r, 64, NF4, P, F16, P + 1, None) == ALIGN
     gb = qmvlib.qmv_gemm_4bit_backward  # dY [M, N] @ W_hat [N, K]
-    assert gb(P, F16, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED    # dY must be bf16
+    assert gb(P, F32, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED    # dY 16-bit only
     assert gb(P, BF16, 8, 48, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # N % 32
     assert gb(P, BF16, 8, 64, 96, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # K % bs
     assert gb(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
