@@ -224,10 +224,13 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
     for (int j = 0; j < NJ; ++j) {
       const int64_t col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
       if (col >= N) continue;
+      // one bias value per column: the fp32 result + fp32(bias[col]), then
+      // one rounding (no addition at all without a bias, so -0 stays -0)
+      const float b = bias ? load_elem<CDT>(bias, col) : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) store_out<CDT>(C, row * N + col, acc[i][j][r], bias, col);
+        if (row < M) store_elem<CDT>(C, row * N + col, bias ? acc[i][j][r] + b : acc[i][j][r]);
       }
     }
 }

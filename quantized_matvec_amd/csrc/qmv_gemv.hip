@@ -532,20 +532,28 @@ __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restr
       const float a = block_scale<DQ>(sc, e0 >> log2bs);
       const uint4 p = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
       const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-      float part[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) part[m] = 0.f;
+      float t[32];
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
         const uint32_t byte = (pw[b >> 2] >> (8 * (b & 3))) & 0xffu;
-        const float t0 = lut[byte >> 4];
-        const float t1 = lut[byte & 15u];
-        const int64_t k = (pc << 5) + 2 * b;
+        t[2 * b] = lut[byte >> 4];
+        t[2 * b + 1] = lut[byte & 15u];
+      }
+      float part[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          part[m] = fmaf(t0, load_elem<XDT>(x, m * K + k), part[m]);
-          part[m] = fmaf(t1, load_elem<XDT>(x, m * K + k + 1), part[m]);
+      for (int m = 0; m < M; ++m) {
+        // the piece's 32 activations of row m as eight 16-byte loads
+        const float4 *xr = reinterpret_cast<const float4 *>(x + m * K + (pc << 5));
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 xv = xr[q];
+          s = fmaf(t[4 * q], xv.x, s);
+          s = fmaf(t[4 * q + 1], xv.y, s);
+          s = fmaf(t[4 * q + 2], xv.z, s);
+          s = fmaf(t[4 * q + 3], xv.w, s);
         }
+        part[m] = s;
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[m] = fmaf(a, part[m], acc[m]);
