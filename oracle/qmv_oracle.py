@@ -75,7 +75,7 @@ __all__ = [
     "quantize_4bit", "mean_fixed_tree", "double_quant", "dequant_absmax",
     "dequantize_4bit", "dequantize_rows", "matmul_4bit", "matmul_4bit_rows",
     "matmul_4bit_backward", "dynamic_tree_table", "quantize_blockwise",
-    "dequantize_blockwise",
+    "dequantize_blockwise", "embedding_4bit",
 ]
 
 NF4_DELTA = 0.9677083      # R1
@@ -391,6 +391,22 @@ def dequantize_rows(packed, absmax_hat, N: int, K: int, blocksize: int,
     a = np.asarray(absmax_hat, dtype=np.float32).reshape(N, K // blocksize)[rows]
     return np.stack([dequantize_4bit(p[i], a[i], K, blocksize, quant_type)
                      for i in range(rows.size)]) if rows.size else np.zeros((0, K), np.float32)
+
+
+# --------------------------------------------------------------------------
+# Embedding4bit (R13)
+# --------------------------------------------------------------------------
+def embedding_4bit(idx, packed, absmax_hat, V: int, D: int, blocksize: int,
+                   quant_type: str = "nf4", out_dtype: str = "fp32"):
+    """R13: "Quantized Embeddings": out[t] = row idx[t] of the dequantized
+    [V, D] table (dequantize_4bit of the flattened table, R7), rounded to the
+    output type; an index outside [0, V) gives a row of zeros."""
+    idx = np.asarray(idx, dtype=np.int64).ravel()
+    W = dequantize_4bit(packed, absmax_hat, V * D, blocksize, quant_type).reshape(V, D)
+    out = np.zeros((idx.size, D), dtype=np.float32)
+    ok = (idx >= 0) & (idx < V)
+    out[ok] = W[idx[ok]]
+    return _cast_out(out, out_dtype)
 
 
 # --------------------------------------------------------------------------

@@ -539,3 +539,43 @@ def test_dequantize_blockwise_is_one_fp32_rounding():
     assert np.array_equal(wb, tb)
     wh = O.dequantize_blockwise(q, absmax, bs, t, "fp16")
     assert np.array_equal(np.asarray(wh).view(np.uint16), w.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------- embedding
+def test_embedding_is_a_one_hot_product():
+    """Gathering rows equals multiplying a one-hot matrix by the dequantized
+    table (the backward's dY @ W_hat): every product is 0 or 1 times a
+    weight, so the float64 sums are exact.  Out-of-range indices are all-zero
+    one-hot rows."""
+    rng = np.random.default_rng(14)
+    V, D, bs = 40, 128, 64
+    W = torch.from_numpy(rng.standard_normal((V, D)) * 0.05).to(torch.bfloat16).to(torch.float64).numpy()
+    packed, absmax = O.quantize_4bit(W, bs, "nf4")
+    idx = np.array([0, 39, 7, 7, -1, 40, 13, 1000, 22])
+    got = O.embedding_4bit(idx, packed, absmax, V, D, bs, "nf4")
+    onehot = np.zeros((idx.size, V))
+    for t, i in enumerate(idx):
+        if 0 <= i < V:
+            onehot[t, i] = 1.0
+    want = O.matmul_4bit_backward(onehot, packed, absmax, V, D, bs, "nf4")
+    assert np.array_equal(got.astype(np.float64), want)
+    assert not got[4].any() and not got[5].any() and not got[7].any()
+
+
+def test_embedding_rows_by_hand_odd_width():
+    """D = 45 (odd): rows start in the middle of a byte and blocks straddle
+    rows; each element is decoded by hand from its byte, nibble and block."""
+    rng = np.random.default_rng(15)
+    V, D, bs = 11, 45, 32
+    W = (rng.standard_normal(V * D) * 0.1).astype(np.float32).astype(np.float64)
+    for qt in ("nf4", "fp4"):
+        packed, absmax = O.quantize_4bit(W, bs, qt)
+        t = O.code_table(qt)
+        idx = np.array([3, 0, 10, 3])
+        got = O.embedding_4bit(idx, packed, absmax, V, D, bs, qt)
+        for r, i in enumerate(idx):
+            for d in range(D):
+                e = i * D + d
+                byte = int(packed[e // 2])
+                code = byte >> 4 if e % 2 == 0 else byte & 15
+                assert got[r, d] == np.float32(t[code] * np.float32(absmax[e // bs]))
