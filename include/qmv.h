@@ -208,6 +208,23 @@ int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_
                            const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
                            qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *stream);
 
+/*
+ * embedding_4bit: rows of a 4-bit quantized embedding table
+ * ("mps-bitsandbytes 0.4.7", "Quantized Embeddings": Embedding4bit,
+ * EmbeddingNF4, EmbeddingFP4).
+ *   W [V, D] quantized as one flat tensor by qmv_quantize_4bit (packed
+ *   [ceil(V * D / 2)], scales for ceil(V * D / blocksize) blocks, plain or
+ *   double-quantized).
+ *   out[t, d] = dequantize_4bit(W)[idx[t], d], bit for bit (fp32(T * a_hat)
+ *   rounded to out_dtype); a row whose index is outside [0, V) is zeros
+ *   (the kernel checks each index; nothing faults).
+ *   idx  [T] device int64, 8-byte aligned;  out [T, D] device row-major, out_dtype
+ * Buffers are the caller's; packed and out 16-byte aligned (QMV_ERR_ALIGNMENT).
+ */
+int qmv_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D, const uint8_t *packed,
+                       const qmv_absmax *scales, int32_t blocksize, qmv_quant_type quant_type,
+                       void *out, qmv_dtype out_dtype, void *stream);
+
 /* Host-side: the 16 fp32 code values the kernels use, by code. */
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]);
 

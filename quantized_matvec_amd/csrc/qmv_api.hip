@@ -294,6 +294,24 @@ int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_
                                                  quant_type, dX, dx_dtype, (hipStream_t)stream));
 }
 
+int qmv_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D, const uint8_t *packed,
+                       const qmv_absmax *scales, int32_t blocksize, qmv_quant_type quant_type,
+                       void *out, qmv_dtype out_dtype, void *stream) {
+  if (!idx || !packed || !out || T <= 0 || V <= 0 || D <= 0 || !valid_qt(quant_type) ||
+      !valid_dtype(out_dtype))
+    return QMV_ERR_INVALID_ARG;
+  if (V > ((int64_t)1 << 62) / D) return QMV_ERR_INVALID_ARG;  // V * D must fit
+  if (!valid_blocksize(blocksize)) return QMV_ERR_UNSUPPORTED;
+  Scales sc;
+  bool dq;
+  const int rc = check_scales(scales, &sc, &dq);
+  if (rc != QMV_OK) return rc;
+  if (reinterpret_cast<uintptr_t>(idx) % 8 != 0 || !aligned16(packed) || !aligned16(out))
+    return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_embedding_4bit(idx, T, V, D, packed, sc, dq, log2_exact(blocksize),
+                                             quant_type, out, out_dtype, (hipStream_t)stream));
+}
+
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]) {
   if (!out16 || !valid_qt(quant_type)) return QMV_ERR_INVALID_ARG;
   const uint32_t *bits = table_bits(quant_type);

@@ -1,0 +1,120 @@
+// embedding_4bit: rows of a 4-bit quantized embedding table
+// ("mps-bitsandbytes 0.4.7", sections "Features" and "Quantized Embeddings":
+// Embedding4bit / EmbeddingNF4 / EmbeddingFP4).
+//
+// The table W [V, D] is quantized as one flat tensor by quantize_4bit
+// (blocks of `blocksize` consecutive elements, two codes per byte, plain or
+// double-quantized scales).  out[t, :] = the dequantized row idx[t], exactly
+// as dequantize_4bit returns those elements: fp32(T[code] * a_hat) rounded to
+// the output type.  An index outside [0, V) yields a row of zeros.
+//
+// A workgroup of 256 threads writes a 2048-element segment of one output row
+// (grid: row segments x output rows).  When D is a multiple of 8, thread t of
+// the segment decodes 8 elements from one 4-byte load (one block: blocks are
+// at least 32 and aligned) and writes them with one 16-byte (or two, fp32)
+// store; otherwise each thread decodes single elements.
+#include <algorithm>
+
+#include "qmv_launch.hpp"
+
+#pragma clang fp contract(off)
+
+namespace qmv {
+
+constexpr int kEmbSeg = 2048;  // elements of a row per workgroup
+
+template <int QT, int ODT, bool DQ, bool VEC>
+__global__ __launch_bounds__(256) void embedding_4bit_kernel(const int64_t *__restrict__ idx,
+                                                             int64_t T, int64_t V, int64_t D,
+                                                             const uint8_t *__restrict__ packed,
+                                                             Scales sc, int log2bs,
+                                                             void *__restrict__ outv) {
+  using OT = typename Storage<ODT>::type;
+  OT *out = static_cast<OT *>(outv);
+  __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
+  const int tid = threadIdx.x;
+  {
+    const uint32_t *tb = table_bits(QT);
+    lut2[tid] = make_float2(__uint_as_float(tb[tid >> 4]), __uint_as_float(tb[tid & 15]));
+  }
+  __syncthreads();
+  const int64_t d0 = (int64_t)blockIdx.x * kEmbSeg;
+
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    const int64_t row = idx[t];                       // the same for the whole workgroup
+    const bool valid = row >= 0 && row < V;
+    OT *dst = out + t * D;
+    if constexpr (VEC) {
+      const int64_t d = d0 + 8 * (int64_t)tid;
+      if (d >= D) continue;
+      float v[8];
+      if (valid) {
+        const int64_t e = row * D + d;                // a multiple of 8: one block, 4 aligned bytes
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(packed + (e >> 1));
+        const float a = block_scale<DQ>(sc, e >> log2bs);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float2 tv = lut2[(w >> (8 * b)) & 0xffu];
+          v[2 * b] = tv.x * a;
+          v[2 * b + 1] = tv.y * a;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
+      if constexpr (ODT == kF32) {
+        float4 *o = reinterpret_cast<float4 *>(dst + d);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        *reinterpret_cast<uint4 *>(dst + d) =
+            make_uint4(cvt_pair<ODT>(v[0], v[1]), cvt_pair<ODT>(v[2], v[3]),
+                       cvt_pair<ODT>(v[4], v[5]), cvt_pair<ODT>(v[6], v[7]));
+      }
+    } else {
+      const int64_t d_end = std::min<int64_t>(D, d0 + kEmbSeg);
+      for (int64_t d = d0 + tid; d < d_end; d += 256) {
+        float v = 0.f;
+        if (valid) {
+          const int64_t e = row * D + d;
+          const uint32_t byte = packed[e >> 1];
+          const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);  // even element: high nibble
+          v = lut2[code * 17u].x * block_scale<DQ>(sc, e >> log2bs);      // entry 17 c = (T[c], T[c])
+        }
+        store_elem<ODT>(dst, d, materialize(v));
+      }
+    }
+  }
+}
+
+template <int QT, int ODT, bool DQ>
+static void launch_emb_t(bool vec, dim3 grid, const int64_t *idx, int64_t T, int64_t V, int64_t D,
+                         const uint8_t *packed, const Scales &sc, int log2bs, void *out,
+                         hipStream_t st) {
+  if (vec)
+    hipLaunchKernelGGL((embedding_4bit_kernel<QT, ODT, DQ, true>), grid, dim3(256), 0, st, idx, T, V,
+                       D, packed, sc, log2bs, out);
+  else
+    hipLaunchKernelGGL((embedding_4bit_kernel<QT, ODT, DQ, false>), grid, dim3(256), 0, st, idx, T,
+                       V, D, packed, sc, log2bs, out);
+}
+
+hipError_t launch_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D,
+                                 const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                 int qt, void *out, int out_dtype, hipStream_t st) {
+  const bool vec = D % 8 == 0;
+  const dim3 grid((unsigned)((D + kEmbSeg - 1) / kEmbSeg), (unsigned)std::min<int64_t>(T, 65535));
+#define QMV_E(QTV, ODTV)                                                                     \
+  if (dq) launch_emb_t<QTV, ODTV, true>(vec, grid, idx, T, V, D, packed, sc, log2bs, out, st); \
+  else launch_emb_t<QTV, ODTV, false>(vec, grid, idx, T, V, D, packed, sc, log2bs, out, st)
+#define QMV_EO(QTV)                                  \
+  if (out_dtype == kF32) { QMV_E(QTV, kF32); }       \
+  else if (out_dtype == kF16) { QMV_E(QTV, kF16); }  \
+  else { QMV_E(QTV, kBF16); }
+  if (qt == kNF4) { QMV_EO(kNF4); } else { QMV_EO(kFP4); }
+#undef QMV_EO
+#undef QMV_E
+  return hipGetLastError();
+}
+
+}  // namespace qmv

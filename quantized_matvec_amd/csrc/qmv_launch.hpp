@@ -73,6 +73,11 @@ hipError_t launch_dequantize_blockwise(const uint8_t *q, const float *absmax, in
                                        const Code2Table &code, void *out, int out_dtype,
                                        hipStream_t st);
 
+// idx: T int64 row indices (device); out [T, D] of out_dtype.
+hipError_t launch_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D,
+                                 const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
+                                 int qt, void *out, int out_dtype, hipStream_t st);
+
 hipError_t launch_gemm_4bit_backward(const void *dY, int dy_dtype, int64_t M, int64_t N, int64_t K,
                                      const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
                                      int qt, void *dX, int dx_dtype, hipStream_t st);

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "qmv_dequantize_blockwise": (ctypes.c_int, [vp, vp, i64, i32, vp, vp, ctypes.c_int, vp]),
         "qmv_gemm_4bit_backward": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
                                                   ctypes.c_int, vp, ctypes.c_int, vp]),
+        "qmv_embedding_4bit": (ctypes.c_int, [vp, i64, i64, i64, vp, ap, i32, ctypes.c_int, vp,
+                                              ctypes.c_int, vp]),
         "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
         "qmv_default_code2": (ctypes.c_int, [vp]),
         "qmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -325,6 +327,32 @@ def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState
                                         ctypes.byref(c), state.blocksize, _QT[state.quant_type],
                                         out.data_ptr(), _DT[out.dtype], _stream(g2)),
            "gemm_4bit_backward")
+    return out
+
+
+def embedding_4bit(idx: torch.Tensor, packed: torch.Tensor, state: QuantState,
+                   out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None):
+    """Rows idx of the 4-bit quantized [V, D] table: out [*idx.shape, D];
+    an index outside [0, V) gives a row of zeros."""
+    if len(state.shape) != 2:
+        raise ValueError("the quantized table must be 2-D [V, D]")
+    V, D = state.shape
+    packed = _dev(packed, "packed")
+    idx = _dev(idx, "idx")
+    if idx.dtype != torch.int64:
+        raise ValueError("idx must be int64")
+    T = idx.numel()
+    shape = tuple(idx.shape) + (D,)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype or state.dtype, device=idx.device)
+    elif not out.is_contiguous() or out.numel() != T * D or out.data_ptr() % 16:
+        raise ValueError("out must be contiguous, 16-byte aligned and hold T * D elements")
+    if T == 0:
+        return out
+    c = state._c()
+    _check(lib().qmv_embedding_4bit(idx.data_ptr(), T, V, D, packed.data_ptr(), ctypes.byref(c),
+                                    state.blocksize, _QT[state.quant_type], out.data_ptr(),
+                                    _DT[out.dtype], _stream(idx)), "embedding_4bit")
     return out
 
 

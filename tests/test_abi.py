@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(qmvlib, n), n
 
@@ -166,3 +166,19 @@ def test_blockwise_preconditions(qmvlib):
     assert fd(P, P2, -5, 64, None, P, F32, None) == INVALID
     assert fd(P, P2, 64, 64, None, P, 3, None) == INVALID
     assert fd(P, P2, 64, 64, None, MIS, BF16, None) == ALIGN
+
+
+def test_embedding_preconditions(qmvlib):
+    f = qmvlib.qmv_embedding_4bit
+    sc = _scales(absmax=P2)
+    r = ctypes.byref(sc)
+    assert f(None, 4, 10, 64, P, r, 64, NF4, P2, BF16, None) == INVALID
+    assert f(P, 0, 10, 64, P, r, 64, NF4, P2, BF16, None) == INVALID
+    assert f(P, 4, 0, 64, P, r, 64, NF4, P2, BF16, None) == INVALID
+    assert f(P, 4, 10, 0, P, r, 64, NF4, P2, BF16, None) == INVALID
+    assert f(P, 4, 1 << 40, 1 << 30, P, r, 64, NF4, P2, BF16, None) == INVALID   # V * D overflows
+    assert f(P, 4, 10, 64, P, r, 48, NF4, P2, BF16, None) == UNSUPPORTED
+    assert f(P, 4, 10, 64, P, r, 64, 3, P2, BF16, None) == INVALID
+    assert f(P, 4, 10, 64, P, None, 64, NF4, P2, BF16, None) == INVALID
+    assert f(P + 4, 4, 10, 64, P, r, 64, NF4, P2, BF16, None) == ALIGN
+    assert f(P, 4, 10, 64, P, r, 64, NF4, MIS, BF16, None) == ALIGN
