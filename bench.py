@@ -13,8 +13,9 @@ HIP events on the launch stream while rotating over distinct weight copies
 (> 512 MB, twice the 256 MB Infinity Cache) so the bytes come from HBM.
 Each kernel is also timed alone, including gemm_4bit_backward (dX = dY @
 W_hat with a bf16 dY [512, 14336]) and the 8-bit blockwise codec on the same
-bf16 weight (blocksize 4096; linear and dynamic-tree tables), which are not
-part of the step.
+bf16 weight (blocksize 4096; linear and dynamic-tree tables) and an
+embedding gather (8192 random rows of a 128256 x 4096 NF4 table to bf16),
+which are not part of the step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -36,6 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 N, K, BS, BS2, M_GEMV, M_GEMM = 14336, 4096, 64, 256, 1, 512
 BS8 = 4096                     # 8-bit blockwise codec block size
+EMB_V, EMB_T = 128256, 8192    # embedding table rows (x K columns) and gathered tokens
 ROTATE_BYTES = 640 << 20       # > 2 x 256 MB Infinity Cache
 
 
@@ -54,6 +56,9 @@ def algorithmic_bytes():
         "quantize_blockwise": 2 * numel + numel + 4 * (numel // BS8),
         "quantize_blockwise_dynamic": 2 * numel + numel + 4 * (numel // BS8),
         "dequantize_blockwise": numel + 4 * (numel // BS8) + 2 * numel,
+        # embedding gather: the gathered rows' codes, scale codes and group
+        # scales, the indices and the bf16 output rows
+        "embedding_4bit": EMB_T * (K // 2 + K // BS + 4 * (K // BS) // BS2 + 8 + 2 * K),
     }
 
 
@@ -292,6 +297,21 @@ def main():
             L.qmv_dequantize_blockwise(q8[i % n_w].data_ptr(), a8[i % n_w].data_ptr(), N * K, BS8, None,
                                        w_ptr[i % n_w], 2, s_h)
 
+        # embedding_4bit: EMB_T random rows of a [EMB_V, K] NF4 table (block 64,
+        # double-quantized scales) to bf16
+        # (the table is drawn on the device: torch's seeded normal generator)
+        g = torch.Generator(device=dev).manual_seed(100 * 4 + 6)
+        E = torch.randn((EMB_V, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        pe, ste = qmv.quantize_4bit(E, BS, "nf4", double_quant=True, blocksize2=BS2)
+        del E
+        eidx = torch.randint(0, EMB_V, (EMB_T,), generator=g, device=dev, dtype=torch.int64)
+        eout = torch.empty(EMB_T, K, dtype=torch.bfloat16, device=dev)
+        ec = ste._c()
+
+        def run_emb(i):
+            L.qmv_embedding_4bit(eidx.data_ptr(), EMB_T, EMB_V, K, pe.data_ptr(), ctypes.byref(ec), BS, 0,
+                                 eout.data_ptr(), 2, s_h)
+
         for name, fn, iters in (("gemv_4bit", run_gemv, kiters), ("gemm_4bit", run_gemm, kiters // 4),
                                 ("gemm_4bit_backward", run_bwd, kiters // 8),
                                 ("dequantize_4bit", run_deq, kiters // 4),
@@ -299,7 +319,8 @@ def main():
                                 ("double_quant", run_dq, kiters // 4),
                                 ("quantize_blockwise", run_q8, kiters // 4),
                                 ("quantize_blockwise_dynamic", lambda i: run_q8(i, tree_p), kiters // 4),
-                                ("dequantize_blockwise", run_dq8, kiters // 4)):
+                                ("dequantize_blockwise", run_dq8, kiters // 4),
+                                ("embedding_4bit", run_emb, kiters // 4)):
             for i in range(5):
                 fn(i)
             kern[name] = timed_loop(fn, iters, stream, torch)
