@@ -812,8 +812,9 @@ hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2
 template <bool DQ>
 __global__ __launch_bounds__(256) void dequantize_absmax_kernel(Scales sc, int64_t n,
                                                                 float *__restrict__ out) {
+  const float offset = DQ ? sc.offset[0] : 0.f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    out[i] = block_scale<DQ>(sc, i);
+    out[i] = block_scale<DQ>(sc, i, offset);
 }
 
 hipError_t launch_dequantize_absmax(const Scales &sc, bool dq, int64_t n, float *out,
@@ -926,11 +927,11 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
   for (int64_t i = (int64_t)blockIdx.x * kDeqThreads + tid; i < nword;
        i += (int64_t)gridDim.x * kDeqThreads) {
     const int64_t e = t0 + 8 * i;
-    emit(e, pk[e >> 3], block_scale<DQ>(sc, e >> log2bs));
+    emit(e, pk[e >> 3], block_scale<DQ>(sc, e >> log2bs, offset));
   }
   if (blockIdx.x == 0 && tid == 0 && (numel & 7)) {
     const int64_t e0 = numel & ~int64_t(7);
-    const float a = block_scale<DQ>(sc, e0 >> log2bs);
+    const float a = block_scale<DQ>(sc, e0 >> log2bs, offset);
     for (int64_t e = e0; e < numel; ++e) {
       const uint32_t byte = packed[e >> 1];
       const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);

@@ -45,9 +45,10 @@ struct Scales {
 };
 
 // Scale of block b.  With double quantization:
-// fp32(fp32(code2[q[b]] * absmax2[b / bs2]) + offset), two roundings.
+// fp32(fp32(code2[q[b]] * absmax2[b / bs2]) + offset), two roundings; the
+// caller reads the offset (s.offset[0]) once, outside its loops.
 template <bool DQ>
-__device__ __forceinline__ float block_scale(const Scales &s, int64_t b) {
+__device__ __forceinline__ float block_scale(const Scales &s, int64_t b, float offset) {
   if constexpr (!DQ) {
     return s.absmax[b];
   } else {
@@ -55,11 +56,10 @@ __device__ __forceinline__ float block_scale(const Scales &s, int64_t b) {
     const float c = s.code2[s.q[b]];
     const float g = s.absmax2[b >> s.log2bs2];
     const float p = c * g;   // rounded to fp32 on its own: never fused with the add
-    return p + s.offset[0];
+    return p + offset;
   }
 }
 
-__device__ __forceinline__ float sc_offset(const Scales &s) { return s.offset[0]; }
 
 // A raw buffer resource over [base, base + bytes): loads past the end return
 // zero and move no data, so range checks need no branch (a branch around a

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(256) void embedding_4bit_kernel(const int64_t *__re
   }
   __syncthreads();
   const int64_t d0 = (int64_t)blockIdx.x * kEmbSeg;
+  const float offset = DQ ? sc.offset[0] : 0.f;
 
   for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
     const int64_t row = idx[t];                       // the same for the whole workgroup
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(256) void embedding_4bit_kernel(const int64_t *__re
       if (valid) {
         const int64_t e = row * D + d;                // a multiple of 8: one block, 4 aligned bytes
         const uint32_t w = *reinterpret_cast<const uint32_t *>(packed + (e >> 1));
-        const float a = block_scale<DQ>(sc, e >> log2bs);
+        const float a = block_scale<DQ>(sc, e >> log2bs, offset);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const float2 tv = lut2[(w >> (8 * b)) & 0xffu];
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void embedding_4bit_kernel(const int64_t *__re
           const int64_t e = row * D + d;
           const uint32_t byte = packed[e >> 1];
           const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);  // even element: high nibble
-          v = lut2[code * 17u].x * block_scale<DQ>(sc, e >> log2bs);      // entry 17 c = (T[c], T[c])
+          v = lut2[code * 17u].x * block_scale<DQ>(sc, e >> log2bs, offset);      // entry 17 c = (T[c], T[c])
         }
         store_elem<ODT>(dst, d, materialize(v));
       }

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
   using PW = typename std::conditional<BPT == 32, uint4, uint2>::type;  // packed bytes per thread
   CT *C = static_cast<CT *>(Cv);
   const CT *bias = static_cast<const CT *>(biasv);
+  const float dq_offset = DQ ? sc.offset[0] : 0.f;  // read once, not per tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
   __shared__ float2 lut2[256];  // packed byte -> (T[byte >> 4], T[byte & 15])
   __shared__ float code2[256];
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
 #pragma unroll
     for (int q = 0; q < 4; ++q) ad[q] = zero_a ? make_uint4(0, 0, 0, 0) : ra[q];
     const bool zero_b = last && BPT * bq >= 32;
-    const float a = zero_b ? 0.f : (DQ ? code2[rsq] * rsa + sc_offset(sc) : rsa);
+    const float a = zero_b ? 0.f : (DQ ? code2[rsq] * rsa + dq_offset : rsa);
     uint32_t pw[BPT / 8];
     __builtin_memcpy(pw, &rb_[SL], sizeof(pw));
     uint32_t o[BPT / 2];
@@ -733,6 +734,7 @@ __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint
   constexpr int RN = 64 / (256 / OCT);  // weight rows per thread: 4 or 2
   using CT = typename Storage<CDT>::type;
   CT *dX = static_cast<CT *>(dXv);
+  const float dq_offset = DQ ? sc.offset[0] : 0.f;  // read once, not per tile
   __shared__ __attribute__((aligned(16))) uint16_t smem_all[G * 2 * kStage];
   __shared__ float2 lut2[256];
   __shared__ float code2[256];
@@ -798,7 +800,7 @@ __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint
 #pragma unroll
     for (int r = 0; r < RN; ++r) {
       const bool zero = last && RN * q + r >= 32;
-      const float a = zero ? 0.f : (DQ ? code2[rsq_[SL][r]] * rsa_[SL][r] + sc_offset(sc) : rsa_[SL][r]);
+      const float a = zero ? 0.f : (DQ ? code2[rsq_[SL][r]] * rsa_[SL][r] + dq_offset : rsa_[SL][r]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float2 tv = lut2[(rb_[SL][r] >> (8 * i)) & 0xffu];

@@ -522,6 +522,7 @@ __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restr
   const int lane = threadIdx.x & 63;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t pieces = K >> 5;  // 16-byte pieces per row
+  const float offset = DQ ? sc.offset[0] : 0.f;
 
   for (int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; n < N; n += nwaves) {
     float acc[M];
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restr
     for (int m = 0; m < M; ++m) acc[m] = 0.f;
     for (int64_t pc = lane; pc < pieces; pc += 64) {
       const int64_t e0 = n * K + (pc << 5);
-      const float a = block_scale<DQ>(sc, e0 >> log2bs);
+      const float a = block_scale<DQ>(sc, e0 >> log2bs, offset);
       const uint4 p = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
       const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
       float t[32];
