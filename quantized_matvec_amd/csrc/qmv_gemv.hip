@@ -505,6 +505,9 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
 
 // Plain fp32 path (fp32 activations): a wave per row, fp32 table values and
 // fp32 multiply-adds.
+constexpr int kF32Rows = 4;    // rows a wave of the fp32 kernel works on together
+constexpr int kF32Pieces = 2;  // 16-byte pieces per lane and row in flight
+
 template <int M, int XDT, int YDT, bool DQ, int QT>
 __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restrict__ xv, int64_t N,
                                                         int64_t K, const uint8_t *__restrict__ packed,
@@ -520,57 +523,83 @@ __global__ __launch_bounds__(256) void gemv_4bit_f32x_kernel(const void *__restr
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const int64_t pieces = K >> 5;  // 16-byte pieces per row
   const float offset = DQ ? sc.offset[0] : 0.f;
 
-  for (int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; n < N; n += nwaves) {
-    float acc[M];
+  // a wave takes RW rows at a time and issues the packed words and scales of
+  // PL pieces per lane of every row before decoding any (addresses clamped,
+  // so the loads are unconditional; a dead slot gets a zero scale).  Each
+  // lane adds its pieces in ascending order, then the wave's lanes are summed.
+  for (int64_t n0 = wave * kF32Rows; n0 < N; n0 += nwaves * kF32Rows) {
+    float acc[kF32Rows][M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.f;
-    for (int64_t pc = lane; pc < pieces; pc += 64) {
-      const int64_t e0 = n * K + (pc << 5);
-      const float a = block_scale<DQ>(sc, e0 >> log2bs, offset);
-      const uint4 p = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
-      const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-      float t[32];
+    for (int r = 0; r < kF32Rows; ++r)
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const uint32_t byte = (pw[b >> 2] >> (8 * (b & 3))) & 0xffu;
-        t[2 * b] = lut[byte >> 4];
-        t[2 * b + 1] = lut[byte & 15u];
-      }
-      float part[M];
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+    for (int64_t pb = 0; pb < pieces; pb += 64 * kF32Pieces) {
+      uint4 pk[kF32Rows][kF32Pieces];
+      float a[kF32Rows][kF32Pieces];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        // the piece's 32 activations of row m as eight 16-byte loads
-        const float4 *xr = reinterpret_cast<const float4 *>(x + m * K + (pc << 5));
-        float s = 0.f;
+      for (int r = 0; r < kF32Rows; ++r) {
+        const int64_t row = n0 + r < N ? n0 + r : N - 1;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 xv = xr[q];
-          s = fmaf(t[4 * q], xv.x, s);
-          s = fmaf(t[4 * q + 1], xv.y, s);
-          s = fmaf(t[4 * q + 2], xv.z, s);
-          s = fmaf(t[4 * q + 3], xv.w, s);
+        for (int p = 0; p < kF32Pieces; ++p) {
+          const int64_t pc = pb + p * 64 + lane;
+          const int64_t e0 = row * K + ((pc < pieces ? pc : pieces - 1) << 5);
+          pk[r][p] = *reinterpret_cast<const uint4 *>(packed + (e0 >> 1));
+          const float sv = block_scale<DQ>(sc, e0 >> log2bs, offset);
+          a[r][p] = (n0 + r < N && pc < pieces) ? sv : 0.f;
         }
-        part[m] = s;
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = fmaf(a, part[m], acc[m]);
+      for (int p = 0; p < kF32Pieces; ++p) {
+        const int64_t pc = pb + p * 64 + lane;
+        const int64_t pcc = pc < pieces ? pc : pieces - 1;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          // the piece's 32 activations of row m as eight 16-byte loads
+          float xv[32];
+          const float4 *xr = reinterpret_cast<const float4 *>(x + m * K + (pcc << 5));
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float4 f = xr[q];
+            xv[4 * q] = f.x;
+            xv[4 * q + 1] = f.y;
+            xv[4 * q + 2] = f.z;
+            xv[4 * q + 3] = f.w;
+          }
+#pragma unroll
+          for (int r = 0; r < kF32Rows; ++r) {
+            const uint32_t pw[4] = {pk[r][p].x, pk[r][p].y, pk[r][p].z, pk[r][p].w};
+            float sum = 0.f;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+              const uint32_t byte = (pw[b >> 2] >> (8 * (b & 3))) & 0xffu;
+              sum = fmaf(lut[byte >> 4], xv[2 * b], sum);
+              sum = fmaf(lut[byte & 15u], xv[2 * b + 1], sum);
+            }
+            acc[r][m] = fmaf(a[r][p], sum, acc[r][m]);
+          }
+        }
+      }
     }
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float v = acc[m];
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      acc[m] = v;
-    }
-    if (lane == 0) {
+    for (int r = 0; r < kF32Rows; ++r) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float v = acc[m];
-        if (bias) v = v + load_elem<YDT>(bias, n);  // one fp32 add, then one rounding
-        store_elem<YDT>(y, m * N + n, v);
+        float v = acc[r][m];
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        acc[r][m] = v;
+      }
+      if (lane == 0 && n0 + r < N) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float v = acc[r][m];
+          if (bias) v = v + load_elem<YDT>(bias, n0 + r);  // one fp32 add, then one rounding
+          store_elem<YDT>(y, m * N + n0 + r, v);
+        }
       }
     }
   }
@@ -583,7 +612,7 @@ template <int M, int YDT>
 static hipError_t launch_f32x_m(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                                 const Scales &sc, bool dq, int log2bs, int qt, void *y,
                                 const void *bias, hipStream_t st) {
-  const unsigned grid = (unsigned)std::min<int64_t>((N + 3) / 4, 1 << 16);
+  const unsigned grid = (unsigned)std::min<int64_t>((N + 4 * kF32Rows - 1) / (4 * kF32Rows), 1 << 16);
 #define QMV_G(DQV, QTV)                                                                       \
   hipLaunchKernelGGL((gemv_4bit_f32x_kernel<M, kF32, YDT, DQV, QTV>), dim3(grid), dim3(256), 0, \
                      st, x, N, K, packed, sc, log2bs, y, bias)
