@@ -339,8 +339,10 @@ def embedding_4bit(idx: torch.Tensor, packed: torch.Tensor, state: QuantState,
     V, D = state.shape
     packed = _dev(packed, "packed")
     idx = _dev(idx, "idx")
+    if idx.dtype in (torch.int32, torch.int16, torch.uint8):
+        idx = idx.to(torch.int64)
     if idx.dtype != torch.int64:
-        raise ValueError("idx must be int64")
+        raise ValueError("idx must be an integer tensor")
     T = idx.numel()
     shape = tuple(idx.shape) + (D,)
     if out is None:
