@@ -616,6 +616,164 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 activations with M > 8: gemm_4bit_f32_kernel
+//
+// C = A @ W_hat^T with fp32 A, the fp32 dequantized weights fp32(T * a_hat)
+// (exactly as dequantize_4bit returns them in fp32), and fp32 products and
+// sums on the fp32 matrix cores: v_mfma_f32_32x32x2_f32, where lane l holds
+// A[l % 32][l / 32] and B[l / 32][l % 32] of a 32 x 2 x 32 step.  A 128 x 128
+// tile of C per workgroup of 4 waves (2 x 2, 64 x 64 each); k-tiles of 32 are
+// staged in LDS as fp32 rows of 33 floats, so the 32 rows x 2 columns an
+// operand read touches fall in 64 different banks.  Two LDS stages: the
+// next tiles' global loads are in flight while the current one is multiplied.
+constexpr int kF32BK = 32;
+constexpr int kF32Ld = kF32BK + 1;
+
+template <int CDT, bool DQ>
+__global__ __launch_bounds__(256, 2) void gemm_4bit_f32_kernel(const float *__restrict__ A, int64_t M,
+                                                               int64_t N, int64_t K,
+                                                               const uint8_t *__restrict__ packed,
+                                                               Scales sc, int log2bs, Table16f table,
+                                                               void *__restrict__ Cv,
+                                                               const void *__restrict__ biasv) {
+  constexpr int BM = 128, BN = 128;
+  constexpr int kStage = (BM + BN) * kF32Ld;  // floats per stage
+  using CT = typename Storage<CDT>::type;
+  CT *C = static_cast<CT *>(Cv);
+  const CT *bias = static_cast<const CT *>(biasv);
+  const float dq_offset = DQ ? sc.offset[0] : 0.f;
+  __shared__ float smem[2 * kStage];
+  __shared__ float lut[16];
+  __shared__ float code2[256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int64_t KT = K / kF32BK;  // K % 32 == 0
+
+  // loader roles: thread t moves row t / 2, columns [16 (t % 2), +16) of the
+  // A tile (four 16-byte loads) and decodes the same span of weight row t / 2
+  // (one 8-byte load; 16 weights lie in one block: blocks are 32 or more)
+  const int lr = tid >> 1, lh = tid & 1;
+  const int64_t arow = m0 + lr < M ? m0 + lr : M - 1;  // rows past M are never stored
+  const int64_t brow = n0 + lr < N ? n0 + lr : N - 1;  // columns past N likewise
+  float4 ra_[2][4];
+  uint2 rb_[2];
+  float rsa_[2];
+  uint32_t rsq_[2];
+  auto load_tile = [&](int64_t kt, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+    const int64_t k = kt * kF32BK + 16 * lh;
+    const float4 *ap = reinterpret_cast<const float4 *>(A + arow * K + k);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra_[SL][q] = ap[q];
+    const int64_t e0 = brow * K + k;
+    rb_[SL] = *reinterpret_cast<const uint2 *>(packed + (e0 >> 1));
+    const int64_t b = e0 >> log2bs;
+    if constexpr (DQ) {
+      rsq_[SL] = sc.q[b];
+      rsa_[SL] = sc.absmax2[b >> sc.log2bs2];
+    } else {
+      rsa_[SL] = sc.absmax[b];
+    }
+  };
+  auto stage_tile = [&](int buf, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+    float *As = smem + buf * kStage;
+    float *Bs = As + BM * kF32Ld;
+    float *ad = As + lr * kF32Ld + 16 * lh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ad[4 * q] = ra_[SL][q].x;
+      ad[4 * q + 1] = ra_[SL][q].y;
+      ad[4 * q + 2] = ra_[SL][q].z;
+      ad[4 * q + 3] = ra_[SL][q].w;
+    }
+    const float a = DQ ? code2[rsq_[SL]] * rsa_[SL] + dq_offset : rsa_[SL];
+    const uint32_t pw[2] = {rb_[SL].x, rb_[SL].y};
+    float *bd = Bs + lr * kF32Ld + 16 * lh;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const uint32_t byte = (pw[bb >> 2] >> (8 * (bb & 3))) & 0xffu;  // even element: high nibble
+      bd[2 * bb] = lut[byte >> 4] * a;
+      bd[2 * bb + 1] = lut[byte & 15u] * a;
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load_tile(0, S0{});
+  load_tile(KT > 1 ? 1 : 0, S1{});
+  if (tid < 16) lut[tid] = table.v[tid];
+  if constexpr (DQ) code2[tid] = sc.code2[tid];
+  __syncthreads();
+  stage_tile(0, S0{});
+  __syncthreads();
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto mma_tile = [&](int buf) {
+    const float *As = smem + buf * kStage;
+    const float *Bs = As + BM * kF32Ld;
+    const int kl = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < kF32BK / 2; ++ks) {
+      float af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = As[(wm * 64 + i * 32 + (lane & 31)) * kF32Ld + 2 * ks + kl];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = Bs[(wn * 64 + j * 32 + (lane & 31)) * kF32Ld + 2 * ks + kl];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // tile kt sits in LDS stage kt % 2 and tile kt + 1 in register set (kt + 1) % 2;
+  // each step loads tile kt + 2 into the register set tile kt used
+  // (loads past the end re-read the last tile, so they are unconditional)
+  auto clampk = [&](int64_t k) { return k < KT ? k : KT - 1; };
+  int64_t kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    load_tile(clampk(kt + 2), S0{});
+    mma_tile(0);
+    stage_tile(1, S1{});
+    __syncthreads();
+    load_tile(clampk(kt + 3), S1{});
+    mma_tile(1);
+    if (kt + 2 < KT) stage_tile(0, S0{});
+    __syncthreads();
+  }
+  if (kt < KT) mma_tile(0);  // odd tile count: the last tile is in stage 0
+
+  // 32 x 32 accumulator layout: column = lane % 32,
+  // row = 8 * (r / 4) + 4 * (lane / 32) + r % 4 for accumulator register r.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+      const float b = bias ? load_elem<CDT>(bias, col) : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) store_elem<CDT>(C, row * N + col, bias ? acc[i][j][r] + b : acc[i][j][r]);
+      }
+    }
+}
+
 template <int ADT>
 static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
                                 const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
@@ -688,18 +846,26 @@ hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, in
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
                             void *C, int c_dtype, const void *bias, hipStream_t st) {
   if (a_dtype == kF32) {
-    // fp32 activations: the fp32 kernel of gemv_4bit (fp32 weights, fp32
-    // products and sums) over slices of 8 rows
-    const size_t csz = c_dtype == kF32 ? 4 : 2;
-    for (int64_t m0 = 0; m0 < M; m0 += 8) {
-      const int rows = (int)std::min<int64_t>(8, M - m0);
-      const hipError_t e = launch_gemv_4bit(static_cast<const float *>(A) + m0 * K, kF32, rows, N, K,
-                                            packed, sc, dq, log2bs, qt,
-                                            static_cast<char *>(C) + (size_t)(m0 * N) * csz, c_dtype,
-                                            bias, st);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    // fp32 activations: up to 8 rows take the fp32 kernel of gemv_4bit, more
+    // the fp32 matrix cores
+    if (M <= 8)
+      return launch_gemv_4bit(A, kF32, (int)M, N, K, packed, sc, dq, log2bs, qt, C, c_dtype, bias, st);
+    Table16f table;
+    const uint32_t *bits = table_bits(qt);
+    for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
+    const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
+    const float *a = static_cast<const float *>(A);
+#define QMV_F(CDT, DQV)                                                                       \
+  hipLaunchKernelGGL((gemm_4bit_f32_kernel<CDT, DQV>), grid, dim3(256), 0, st, a, M, N, K, packed, \
+                     sc, log2bs, table, C, bias)
+#define QMV_FD(CDT) \
+  if (dq) { QMV_F(CDT, true); } else { QMV_F(CDT, false); }
+    if (c_dtype == kF32) { QMV_FD(kF32); }
+    else if (c_dtype == kF16) { QMV_FD(kF16); }
+    else { QMV_FD(kBF16); }
+#undef QMV_FD
+#undef QMV_F
+    return hipGetLastError();
   }
   if (a_dtype == kF16) return launch_gemm_t<kF16>(A, M, N, K, packed, sc, dq, log2bs, qt, C, c_dtype, bias, st);
   return launch_gemm_t<kBF16>(A, M, N, K, packed, sc, dq, log2bs, qt, C, c_dtype, bias, st);

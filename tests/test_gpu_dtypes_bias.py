@@ -128,11 +128,12 @@ def test_backward_fp16(M):
 
 
 # ---------------------------------------------------------------- fp32 activations
-@pytest.mark.parametrize("M", [1, 8, 9, 20])
+@pytest.mark.parametrize("M", [1, 8, 9, 20, 129, 300])
 @pytest.mark.parametrize("od", ["fp32", "bf16"])
 def test_gemm_fp32_parity(M, od):
-    """fp32 A: fp32 weights and sums, 8 rows per pass (9 and 20 rows end on
-    partial passes)."""
+    """fp32 A: fp32 weights, products and sums (up to 8 rows on the fp32 gemv
+    kernel, more on the fp32 matrix cores in 128 x 128 tiles: 129 and 300
+    end on partial row tiles, N = 200 on a partial column tile)."""
     N, K, bs = 200, 512, 64
     W = synth.gaussian((N, K), 0.02, 350 + M, "fp32")
     A = synth.gaussian((M, K), 1.0, 351 + M, "fp32")
@@ -155,7 +156,7 @@ CASES = [  # (entry, x dtype, M): the kernel each one reaches
     ("gemm", "bf16", 12),   # narrow
     ("gemm", "fp16", 40),   # split-K
     ("gemm", "bf16", 130),  # tile
-    ("gemm", "fp32", 11),   # fp32 slices
+    ("gemm", "fp32", 11),   # fp32 matrix cores
 ]
 
 
@@ -187,3 +188,19 @@ def test_bias_wrong_shape_is_refused():
         qmv.gemv_4bit(x, packed, st, bias=torch.zeros(N + 1, dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError):
         qmv.gemv_4bit(x, packed, st, bias=torch.zeros(N, dtype=torch.float32, device="cuda"))
+
+
+@pytest.mark.parametrize("rows", [9, 128, 200])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemm_fp32_identity_rows_exact(rows, dq):
+    """Identity rows of fp32 A return the fp32 dequantized weight rows bit for
+    bit: each output is 1 * w plus exact zeros."""
+    N, K, bs = 300, 256, 64
+    W = synth.gaussian((N, K), 0.02, 380 + rows, "fp32")
+    p_ref, ahat = oracle_state(f64(W), bs, "nf4", dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "nf4", double_quant=dq)
+    A = torch.eye(K, dtype=torch.float32)[:rows].cuda()
+    C = qmv.gemm_4bit(A, packed, st, out_dtype=torch.float32).cpu().numpy()
+    What = O.dequantize_4bit(p_ref, ahat, N * K, bs, "nf4").reshape(N, K)
+    want = np.ascontiguousarray(What[:, :rows].T) + np.float32(0)   # -0 reads as +0
+    assert np.array_equal(C.view(np.uint32), want.view(np.uint32))
