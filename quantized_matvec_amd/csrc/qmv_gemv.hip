@@ -91,6 +91,12 @@ __device__ __forceinline__ void store_y(void *y, int ydt, int64_t i, float v, co
   else static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_f16_rne(v);
 }
 
+__device__ __forceinline__ float bias_value(const void *bias, int ydt, int64_t n) {
+  if (ydt == kF32) return static_cast<const float *>(bias)[n];
+  if (ydt == kBF16) return bits16_to_f32<kBF16>(static_cast<const uint16_t *>(bias)[n]);
+  return bits16_to_f32<kF16>(static_cast<const uint16_t *>(bias)[n]);
+}
+
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_move(float x) {  // rows outside ROW_MASK read 0
   return __builtin_bit_cast(
@@ -272,40 +278,40 @@ __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSim
 // ---------------------------------------------------------------------------
 // M = 1 (the decode step): gemv_4bit_m1_kernel
 //
-// Same table and per-wave row ranges as above, organised for the smallest
-// vector-instruction count per 16-byte piece:
-//  * The work of a wave is a sequence of steps (row group g, slice s); a step
-//    covers RPS rows (1, 2 or 4, unrolled) of one slice.  D steps per wave
-//    are in flight: the loads of step t + D are issued right after step t is
-//    decoded.
-//  * Every load is a buffer load whose resource (base, size) is computed with
-//    scalar instructions per step; the lane's part of the address is a
-//    constant register.  A padding row, a lane past the row's last piece or
-//    (in the prologue of a short wave) a step past the end gets a zero-sized
-//    range: the load returns zeros and moves no data.  In the steady-state
-//    loop every refill is live and unconditional, so the compiler waits for
-//    exactly the step it is about to decode.
+// Same table as above, one 1024-thread workgroup per CU, organised for the
+// smallest vector-instruction count per 16-byte piece and an even load:
+//  * The unit of work is an item: one slice (64 lanes x 16 bytes, 2048
+//    weights) of one output row.  A wave owns a contiguous run of rows and
+//    walks its items row by row, slice by slice.  The loads of the next item
+//    are issued before the current one is decoded, so one item per wave is
+//    in flight while it decodes (measured faster than 2-4 items in flight:
+//    deeper queues leave loaded data waiting behind the decode).
+//  * Runs are dealt so that the ones holding an extra row (when the rows do
+//    not divide evenly) are spread over all workgroups: wave slot i of
+//    workgroup b takes run i * gridDim.x + b.  Each wave stops after its own
+//    last item.
+//  * Every load is a buffer load whose range covers exactly the item's live
+//    bytes (weights, block codes, group scales); a lane past the row's last
+//    piece, or an item past the run's end, reads zeros and moves no data.
 //  * The activation vector is staged once in LDS (when it fits), transposed
-//    so that a slice's 64 lanes read consecutive 16-byte chunks.
+//    so that a slice's 64 lanes read consecutive 16-byte chunks.  With 1 to 4
+//    slices per row every lane then keeps its chunks of all slices in
+//    registers; otherwise it reads the current slice's chunks per item.
 // ---------------------------------------------------------------------------
 constexpr int kM1Threads = 1024;
-// Steps in flight per wave, by rows per step: 4 pieces (4 KB) per wave for
-// RPS = 4 and 2, 2 pieces for RPS = 1.  With 16 waves per CU this keeps about
-// 32-64 KB of weight loads outstanding per CU; deeper queues stall the
-// issuing waves (the memory pipeline is full) while loaded data waits to be
-// decoded, and measured slower on every layer shape.
-template <int RPS>
-constexpr int m1_depth() { return RPS == 4 ? 1 : 2; }
 constexpr int kM1XLdsBytes = 90112;  // activations staged in LDS up to K = 45056 (whole slices)
 
-
-template <int XDT, bool DQ, int XC, int RPS>  // XC: x chunks staged per thread (0: no staging)
-__global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
+// XC: x chunks staged per thread (0: no staging); SX: slices per row held in
+// registers (0: none); UG: every item's blocks share one double-quant group
+// (rows a multiple of 2048 weights and a slice's blocks no more than a
+// group), so the group scale has a wave-uniform address
+template <int XDT, bool DQ, int XC, int SX, bool UG>
+__global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
     const uint16_t *__restrict__ x, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
     int rows_rem, const void *__restrict__ bias) {
   constexpr bool XLDS = XC > 0;
-  constexpr int D = m1_depth<RPS>();  // steps in flight
+  static_assert(SX == 0 || XLDS, "register-held activations are read from the staged copy");
   // one LDS block with the code-pair table at address 0, so a lookup address
   // needs no base added; then the DQ table and the staged activations
   __shared__ __attribute__((aligned(16))) uint32_t lds[256 * kLutReplicas + 256 +
@@ -315,28 +321,26 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
   uint16_t *xl = reinterpret_cast<uint16_t *>(lds + 256 * kLutReplicas + 256);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave-uniform: keeps the step bookkeeping in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kM1Threads / 64) + (tid >> 6));
-  const int64_t r_begin = (int64_t)wave * rows_per_wave + (wave < rows_rem ? wave : rows_rem);
-  const int64_t nrows = rows_per_wave + (wave < rows_rem ? 1 : 0);
+  // run of this wave (wave-uniform, so the bookkeeping stays in scalar registers)
+  const int run = __builtin_amdgcn_readfirstlane((tid >> 6) * (int)gridDim.x + (int)blockIdx.x);
+  const int64_t r_begin = (int64_t)run * rows_per_wave + (run < rows_rem ? run : rows_rem);
+  const int64_t nrows = rows_per_wave + (run < rows_rem ? 1 : 0);
   const int64_t pieces = K >> 5;
-  const int S = (int)((pieces + 63) >> 6);
-  const int64_t T = (nrows + RPS - 1) / RPS * S;  // steps of this wave
-  const int64_t half_k = K >> 1;
-  const int bs_shift = log2bs - 5;                // blocks per lane piece: lane >> bs_shift
-  const uint32_t lane_w = (uint32_t)lane << 4;    // byte offset of the lane's piece
-  const uint32_t lane_b = (uint32_t)lane >> bs_shift;  // block offset of the lane's piece
-  // blocks a slice touches (one when a block is longer than a slice)
-  const uint32_t blocks_per_slice = bs_shift > 6 ? 1u : 64u >> bs_shift;
+  const int S = SX > 0 ? SX : (int)((pieces + 63) >> 6);  // slices per row
+  const int64_t T = nrows * S;                             // items of this wave
+  const int bs_shift = log2bs - 5;                         // blocks per piece: lane >> bs_shift
+  const uint32_t lane_w = (uint32_t)lane << 4;             // byte offset of the lane's piece
+  const uint32_t lane_b = (uint32_t)lane >> bs_shift;      // block offset of the lane's piece
 
   // Prologue loads, oldest first: staged activations, the DQ table, then the
-  // queue.  Loads return in order, so the staging waits only for its own.
+  // first item.  Loads return in order, so the staging waits only for its own.
   const int nch = (int)(K >> 3);  // 16-byte chunks of x
   uint4 xch[XC > 0 ? XC : 1];
 #pragma unroll
   for (int i = 0; i < XC; ++i) {
     const int c = i * kM1Threads + tid;
-    xch[i] = reinterpret_cast<const uint4 *>(x)[c < nch ? c : nch - 1];
+    xch[i] = make_uint4(0, 0, 0, 0);
+    if (c < nch) xch[i] = reinterpret_cast<const uint4 *>(x)[c];
   }
   float c2v = 0.f, offset = 0.f;
   if constexpr (DQ) {
@@ -344,55 +348,51 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
     offset = sc.offset[0];
   }
 
-  uint4v w[D][RPS];
-  float sa[D][RPS];
-  uint32_t sq[D][RPS];
-  // step cursor (row group g, slice s), wave-uniform
-  struct Step {
-    int64_t g;
-    int s;
-  };
-  auto next = [&](Step &c) {
-    if (++c.s == S) {
-      c.s = 0;
-      ++c.g;
+  uint4v w[2];
+  float sa[2];
+  uint8_t sq[2];
+  // issue the loads of item (row rr of the run, slice s) into slot j
+  auto issue = [&](int64_t rr, int s, bool live, int j) {
+    const int64_t row = r_begin + (live ? rr : 0);
+    const int64_t e0 = row * K + (int64_t)s * 2048;  // first weight of the item
+    const int64_t left = K - (int64_t)s * 2048;
+    const int64_t ne = left < 2048 ? left : 2048;   // live weights of the item
+    w[j] = __builtin_amdgcn_raw_buffer_load_b128(
+        make_rsrc(packed + (e0 >> 1), live ? (uint32_t)(ne >> 1) : 0u), lane_w, 0, 0);
+    const int64_t ub = e0 >> log2bs;             // block of the first weight
+    const int64_t ue = (e0 + ne - 1) >> log2bs;  // block of the last weight
+    const uint32_t nbl = live ? (uint32_t)(ue - ub + 1) : 0u;
+    if constexpr (DQ && UG) {
+      sq[j] = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(sc.q + ub, nbl), lane_b, 0, 0);
+      sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           make_rsrc(sc.absmax2 + (ub >> sc.log2bs2), live ? 4u : 0u),
+                                           0, 0, 0));
+    } else if constexpr (DQ) {
+      sq[j] = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(sc.q + ub, nbl), lane_b, 0, 0);
+      const int64_t g0 = ub >> sc.log2bs2;
+      const uint32_t ng = live ? (uint32_t)((ue >> sc.log2bs2) - g0 + 1) : 0u;
+      const uint32_t gl = ((uint32_t)(ub & ((1 << sc.log2bs2) - 1)) + lane_b) >> sc.log2bs2;
+      sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           make_rsrc(sc.absmax2 + g0, ng << 2), gl << 2, 0, 0));
+    } else {
+      sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           make_rsrc(sc.absmax + ub, nbl << 2), lane_b << 2, 0, 0));
     }
   };
-  auto issue = [&](const Step &c, bool step_live, int j) {
-    const int64_t g = c.g;
-    const int s = c.s;
-    const int64_t live_pieces = pieces - (int64_t)s * 64;
-    const uint32_t wbytes = (uint32_t)((live_pieces < 64 ? live_pieces : 64) << 4);
-#pragma unroll
-    for (int r = 0; r < RPS; ++r) {
-      const int64_t rr = g * RPS + r;
-      const bool live = step_live && rr < nrows;
-      const int64_t row = r_begin + (live ? rr : 0);
-      const int64_t e0 = row * K + (int64_t)s * 2048;  // first weight of the row's slice
-      w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(
-          make_rsrc(packed + (e0 >> 1), live ? wbytes : 0u), lane_w, 0, 0);
-      const int64_t ub = e0 >> log2bs;  // first block of the row's slice
-      const uint32_t nbl = live ? blocks_per_slice : 0u;
-      if constexpr (DQ) {
-        sq[j][r] = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(sc.q + ub, nbl), lane_b, 0, 0);
-        const int64_t g0 = ub >> sc.log2bs2;
-        const uint32_t gl = ((uint32_t)(ub & ((1 << sc.log2bs2) - 1)) + lane_b) >> sc.log2bs2;
-        sa[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 make_rsrc(sc.absmax2 + g0, live ? 256u : 0u),
-                                                 gl << 2, 0, 0));
-      } else {
-        sa[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 make_rsrc(sc.absmax + ub, nbl << 2), lane_b << 2,
-                                                 0, 0));
-      }
-    }
-  };
-
-  Step ci = {0, 0};  // next step to issue
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    issue(ci, j < T, j);
-    next(ci);
+  issue(0, 0, T > 0, 0);
+  // the bias of the run's first 64 rows, lane i holding row i's, read ahead
+  // of every item so that finishing a row never waits on a new load
+  // (raw bits, through a bounded buffer load: no branch, so no wait here)
+  uint32_t bias_run = 0;
+  {
+    const int64_t nb = bias ? (nrows < 64 ? nrows : 64) : 0;
+    if (ydt == kF32)
+      bias_run = __builtin_amdgcn_raw_buffer_load_b32(
+          make_rsrc(static_cast<const float *>(bias) + r_begin, (uint32_t)(nb * 4)), lane * 4, 0, 0);
+    else
+      bias_run = __builtin_amdgcn_raw_buffer_load_b16(
+          make_rsrc(static_cast<const uint16_t *>(bias) + r_begin, (uint32_t)(nb * 2)), lane * 2, 0,
+          0);
   }
 
   if constexpr (XLDS) {
@@ -416,89 +416,121 @@ __global__ __launch_bounds__(kM1Threads, 4) void gemv_4bit_m1_kernel(
   __syncthreads();
   const uint32_t lane_sel = (uint32_t)lane << 2;
   const char *lut_bytes = reinterpret_cast<const char *>(lut);
+  const uint4v *xlv = reinterpret_cast<const uint4v *>(xl);
 
-  float acc[RPS];
+  // activations of every slice, when they stay in registers
+  uint4v xr[SX > 0 ? SX : 1][4];
 #pragma unroll
-  for (int r = 0; r < RPS; ++r) acc[r] = 0.f;
-  uint4v xs[4];
-  int xs_slice = -1;
+  for (int s = 0; s < SX; ++s)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xr[s][q] = xlv[s * 256 + q * 64 + lane];
 
-  auto compute = [&](const Step &c, int j) {
-    const int64_t g = c.g;
-    const int s = c.s;
-    if (s != xs_slice) {  // activations of this slice (wave-uniform)
-      xs_slice = s;
-      if constexpr (XLDS) {
-        const uint4v *xp = reinterpret_cast<const uint4v *>(xl) + s * 256 + lane;
+  // sum over the item of T[code] * x, before the block scale
+  auto decode = [&](const uint4v &wd, const uint4v *xq) {
+    float part = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xs[q] = xp[q * 64];
+    for (int bb = 0; bb < 16; ++bb) {
+      const uint32_t addr =
+          __builtin_amdgcn_perm(wd[bb >> 2], lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
+      const uint32_t xv = xq[bb >> 2][bb & 3];
+      part = dot2<XDT>(*reinterpret_cast<const uint32_t *>(lut_bytes + addr), xv, part);
+    }
+    return part;
+  };
+  auto finish_row = [&](int64_t rr, float acc) {
+    float v = wave_sum(acc);
+    const int64_t n = r_begin + rr;
+    if (bias) {
+      float b;
+      if (rr < 64) {
+        const uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)bias_run, (int)rr);
+        b = ydt == kF32 ? __builtin_bit_cast(float, bits)
+                        : (ydt == kBF16 ? bits16_to_f32<kBF16>(bits) : bits16_to_f32<kF16>(bits));
       } else {
-        // a lane past the row's last piece multiplies its (zero) codes by
-        // zero activations, so it adds nothing
-        const int64_t pc = (int64_t)s * 64 + lane;
-        const uint4v *xp = reinterpret_cast<const uint4v *>(x + ((pc < pieces ? pc : 0) << 5));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xs[q] = pc < pieces ? xp[q] : uint4v{0, 0, 0, 0};
+        b = bias_value(bias, ydt, n);
       }
+      v = v + b;
     }
-#pragma unroll
-    for (int r = 0; r < RPS; ++r) {
-      if (g * RPS + r < nrows) {  // wave-uniform
-        const uint4v wd = w[j][r];
-        float part = 0.f;
-#pragma unroll
-        for (int bb = 0; bb < 16; ++bb) {
-          const uint32_t addr =
-              __builtin_amdgcn_perm(wd[bb >> 2], lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
-          part = dot2<XDT>(*reinterpret_cast<const uint32_t *>(lut_bytes + addr), xs[bb >> 2][bb & 3],
-                           part);
-        }
-        const float ahat = DQ ? code2[sq[j][r]] * sa[j][r] + offset : sa[j][r];
-        acc[r] = fmaf(ahat, part, acc[r]);
-      }
-    }
-    if (s == S - 1) {  // the rows of group g are complete
-#pragma unroll
-      for (int r = 0; r < RPS; ++r) {
-        if (g * RPS + r < nrows) {
-          const float v = wave_sum(acc[r]);
-          if (lane == r) store_y(y, ydt, r_begin + g * RPS + r, v, bias, r_begin + g * RPS + r);
-        }
-        acc[r] = 0.f;
+    if (lane == 0) {
+      if (ydt == kF32) {
+        static_cast<float *>(y)[n] = v;
+      } else {  // both roundings computed, one selected: no branch
+        const uint32_t h = ydt == kBF16 ? f32_to_bf16_rne(v) : f32_to_f16_rne(v);
+        static_cast<uint16_t *>(y)[n] = (uint16_t)h;
       }
     }
   };
 
-  // steady state: every refill is a live step, so the loads are unconditional
-  // and each decode waits for exactly its own step
-  Step cc = {0, 0};  // next step to decode
-  int64_t t0 = 0;
-  for (; t0 + 2 * D <= T; t0 += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      compute(cc, j);
-      next(cc);
-      issue(ci, true, j);
-      next(ci);
+  // block scale of an item's piece.  The code byte passes through an empty
+  // asm statement where it is used, so no arithmetic on it is hoisted ahead
+  // of the next item's loads (which would wait for this item's data first).
+  auto item_scale = [&](uint8_t q8, float a) {
+    if constexpr (DQ) {
+      return code2[q8] * a + offset;
+    } else {
+      return a;
     }
-  }
-  // drain: fewer than 2 D steps left
+  };
+
+  float acc = 0.f;
+  if constexpr (SX > 0) {
+    // slot and slice of every step known at compile time: unroll lcm(2, SX)
+    constexpr int U = SX == 3 ? 6 : (SX == 1 ? 2 : SX);
+    for (int64_t t0 = 0; t0 < T; t0 += U) {
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    if (t0 + j < T) {
-      compute(cc, j);
-      next(cc);
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + u;
+        if (t >= T) break;
+        const int j = u & 1, s = u % SX;
+        issue((t + 1) / SX, (u + 1) % SX, t + 1 < T, j ^ 1);
+        const float ahat = item_scale(sq[j], sa[j]);
+        acc = fmaf(ahat, decode(w[j], xr[s]), acc);
+        if (s == SX - 1) {
+          finish_row(t / SX, acc);
+          acc = 0.f;
+        }
+      }
     }
-    if (t0 + j + D < T) {
-      issue(ci, true, j);
-      next(ci);
+  } else {
+    int64_t rd = 0, rn = 0;  // row (within the run) of the item decoded / issued next
+    int sd = 0, sn = 1;      // and its slice
+    if (sn == S) {
+      sn = 0;
+      ++rn;
     }
-  }
+    for (int64_t t0 = 0; t0 < T; t0 += 2) {
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    if (t0 + D + j < T) {
-      compute(cc, j);
-      next(cc);
+      for (int j = 0; j < 2; ++j) {
+        const int64_t t = t0 + j;
+        if (t >= T) break;
+        issue(rn, sn, t + 1 < T, j ^ 1);
+        if (++sn == S) {
+          sn = 0;
+          ++rn;
+        }
+        uint4v xq[4];
+        if constexpr (XLDS) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xq[q] = xlv[sd * 256 + q * 64 + lane];
+        } else {
+          // a lane past the row's last piece multiplies its (zero) codes by
+          // zero activations, so it adds nothing
+          const int64_t pc = (int64_t)sd * 64 + lane;
+          const uint4v *xp = reinterpret_cast<const uint4v *>(x + ((pc < pieces ? pc : 0) << 5));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xq[q] = pc < pieces ? xp[q] : uint4v{0, 0, 0, 0};
+        }
+        const float ahat = item_scale(sq[j], sa[j]);
+        acc = fmaf(ahat, decode(w[j], xq), acc);
+        if (sd == S - 1) {
+          finish_row(rd, acc);
+          acc = 0.f;
+        }
+        if (++sd == S) {
+          sd = 0;
+          ++rd;
+        }
+      }
     }
   }
 }
@@ -712,33 +744,41 @@ static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *
   const int64_t need = (slices * 256 + kM1Threads - 1) / kM1Threads;
   const int xc =
       slices * 4096 > kM1XLdsBytes ? 0 : (need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 6);
-  // rows decoded together: as many as a wave has, up to 4
-  const double avg_rows = (double)N / (double)total_waves;
-  const int rps = avg_rows >= 3.0 ? 4 : (avg_rows >= 1.5 ? 2 : 1);
-#define QMV_M1(DQV, XCV, RV)                                                                   \
-  hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, RV>), dim3((unsigned)grid),          \
+  // slices per row held in registers: all of them, for 1 to 4 slices
+  const int sx = (xc > 0 && slices <= 4) ? (int)slices : 0;
+  // one double-quant group per item: whole slices, and a slice's blocks
+  // (2048 / blocksize, at least one) within a group
+  const int64_t slice_blocks = log2bs >= 11 ? 1 : (int64_t)1 << (11 - log2bs);
+  const bool ug = dq && K % 2048 == 0 && slice_blocks <= ((int64_t)1 << sc.log2bs2);
+#define QMV_M1(DQV, XCV, SV)                                                                   \
+  if (ug)                                                                                      \
+    hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, SV, DQV>), dim3((unsigned)grid),   \
+                       dim3(kM1Threads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt,  \
+                       rpw, rem, bias);                                                        \
+  else                                                                                         \
+  hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, SV, false>), dim3((unsigned)grid),   \
                      dim3(kM1Threads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt, rpw, \
                      rem, bias)
-#define QMV_M1R(DQV, XCV)                                          \
-  switch (rps) {                                                   \
-    case 4: QMV_M1(DQV, XCV, 4); break;                            \
-    case 2: QMV_M1(DQV, XCV, 2); break;                            \
-    default: QMV_M1(DQV, XCV, 1); break;                           \
-  }
-#define QMV_M1X(DQV)                        \
-  switch (xc) {                             \
-    case 0: QMV_M1R(DQV, 0); break;         \
-    case 1: QMV_M1R(DQV, 1); break;         \
-    case 2: QMV_M1R(DQV, 2); break;         \
-    case 4: QMV_M1R(DQV, 4); break;         \
-    default: QMV_M1R(DQV, 6); break;        \
+#define QMV_M1X(DQV)                                   \
+  switch (sx) {                                        \
+    case 1: QMV_M1(DQV, 1, 1); break;                  \
+    case 2: QMV_M1(DQV, 1, 2); break;                  \
+    case 3: QMV_M1(DQV, 1, 3); break;                  \
+    case 4: QMV_M1(DQV, 1, 4); break;                  \
+    default:                                           \
+      switch (xc) {                                    \
+        case 0: QMV_M1(DQV, 0, 0); break;              \
+        case 1: QMV_M1(DQV, 1, 0); break;              \
+        case 2: QMV_M1(DQV, 2, 0); break;              \
+        case 4: QMV_M1(DQV, 4, 0); break;              \
+        default: QMV_M1(DQV, 6, 0); break;             \
+      }                                                \
   }
   if (dq) {
     QMV_M1X(true);
   } else {
     QMV_M1X(false);
   }
-#undef QMV_M1R
 #undef QMV_M1X
 #undef QMV_M1
   return hipGetLastError();
