@@ -461,9 +461,9 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
     }
   };
 
-  // block scale of an item's piece.  The code byte passes through an empty
-  // asm statement where it is used, so no arithmetic on it is hoisted ahead
-  // of the next item's loads (which would wait for this item's data first).
+  // block scale of an item's piece.  The code byte stays 8 bits wide until
+  // here: widened where it is loaded, the widening would be hoisted ahead of
+  // the loop and wait for the first item's loads before the second is issued.
   auto item_scale = [&](uint8_t q8, float a) {
     if constexpr (DQ) {
       return code2[q8] * a + offset;
