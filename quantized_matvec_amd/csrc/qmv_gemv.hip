@@ -305,7 +305,9 @@ constexpr int kM1XLdsBytes = 90112;  // activations staged in LDS up to K = 4505
 // registers (0: none); UG: every item's blocks share one double-quant group
 // (rows a multiple of 2048 weights and a slice's blocks no more than a
 // group), so the group scale has a wave-uniform address
-template <int XDT, bool DQ, int XC, int SX, bool UG>
+// MR: rows of activations (1 to 4): one table lookup per packed byte serves
+// all of them.
+template <int XDT, bool DQ, int XC, int SX, bool UG, int MR>
 __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
     const uint16_t *__restrict__ x, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     Scales sc, int log2bs, Table16 table, void *__restrict__ y, int ydt, int rows_per_wave,
@@ -334,13 +336,16 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
 
   // Prologue loads, oldest first: staged activations, the DQ table, then the
   // first item.  Loads return in order, so the staging waits only for its own.
-  const int nch = (int)(K >> 3);  // 16-byte chunks of x
+  // staged chunk c: activation row c / (S * 256), chunk c % (S * 256) of it
+  const int nch = (int)(K >> 3);  // 16-byte chunks of an activation row
+  const int rch = S * 256;        // staged chunks per activation row (whole slices)
   uint4 xch[XC > 0 ? XC : 1];
 #pragma unroll
   for (int i = 0; i < XC; ++i) {
     const int c = i * kM1Threads + tid;
+    const int m = c / rch, cr = c - m * rch;
     xch[i] = make_uint4(0, 0, 0, 0);
-    if (c < nch) xch[i] = reinterpret_cast<const uint4 *>(x)[c];
+    if (m < MR && cr < nch) xch[i] = reinterpret_cast<const uint4 *>(x + (int64_t)m * K)[cr];
   }
   float c2v = 0.f, offset = 0.f;
   if constexpr (DQ) {
@@ -403,10 +408,9 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       const int c = i * kM1Threads + tid;
-      const int pc = c >> 2, q = c & 3;
-      if (c < S * 256)
-        reinterpret_cast<uint4 *>(xl)[(((pc >> 6) << 2) + q) * 64 + (pc & 63)] =
-            c < nch ? xch[i] : make_uint4(0, 0, 0, 0);
+      const int m = c / rch, cr = c - m * rch;
+      const int pc = cr >> 2, q = cr & 3;
+      if (m < MR) reinterpret_cast<uint4 *>(xl)[m * rch + (((pc >> 6) << 2) + q) * 64 + (pc & 63)] = xch[i];
     }
   }
   if constexpr (DQ) {
@@ -419,29 +423,34 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
   const uint4v *xlv = reinterpret_cast<const uint4v *>(xl);
 
   // activations of every slice, when they stay in registers
-  uint4v xr[SX > 0 ? SX : 1][4];
+  uint4v xr[SX > 0 ? MR : 1][SX > 0 ? SX : 1][4];
 #pragma unroll
-  for (int s = 0; s < SX; ++s)
+  for (int m = 0; m < (SX > 0 ? MR : 0); ++m)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xr[s][q] = xlv[s * 256 + q * 64 + lane];
+    for (int s = 0; s < SX; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xr[m][s][q] = xlv[m * rch + s * 256 + q * 64 + lane];
 
-  // sum over the item of T[code] * x, before the block scale
-  auto decode = [&](const uint4v &wd, const uint4v *xq) {
-    float part = 0.f;
+  // sums over the item of T[code] * x, before the block scale, into part[m]
+  auto decode = [&](const uint4v &wd, const uint4v (*xq)[4], float *part) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) part[m] = 0.f;
 #pragma unroll
     for (int bb = 0; bb < 16; ++bb) {
       const uint32_t addr =
           __builtin_amdgcn_perm(wd[bb >> 2], lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
-      const uint32_t xv = xq[bb >> 2][bb & 3];
-      part = dot2<XDT>(*reinterpret_cast<const uint32_t *>(lut_bytes + addr), xv, part);
+      const uint32_t tv = *reinterpret_cast<const uint32_t *>(lut_bytes + addr);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const uint32_t xv = xq[m][bb >> 2][bb & 3];
+        part[m] = dot2<XDT>(tv, xv, part[m]);
+      }
     }
-    return part;
   };
-  auto finish_row = [&](int64_t rr, float acc) {
-    float v = wave_sum(acc);
+  auto finish_row = [&](int64_t rr, const float *acc) {
     const int64_t n = r_begin + rr;
+    float b = 0.f;
     if (bias) {
-      float b;
       if (rr < 64) {
         const uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)bias_run, (int)rr);
         b = ydt == kF32 ? __builtin_bit_cast(float, bits)
@@ -449,14 +458,18 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
       } else {
         b = bias_value(bias, ydt, n);
       }
-      v = v + b;
     }
-    if (lane == 0) {
-      if (ydt == kF32) {
-        static_cast<float *>(y)[n] = v;
-      } else {  // both roundings computed, one selected: no branch
-        const uint32_t h = ydt == kBF16 ? f32_to_bf16_rne(v) : f32_to_f16_rne(v);
-        static_cast<uint16_t *>(y)[n] = (uint16_t)h;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float v = wave_sum(acc[m]);
+      if (bias) v = v + b;
+      if (lane == m) {
+        if (ydt == kF32) {
+          static_cast<float *>(y)[m * N + n] = v;
+        } else {  // both roundings computed, one selected: no branch
+          const uint32_t h = ydt == kBF16 ? f32_to_bf16_rne(v) : f32_to_f16_rne(v);
+          static_cast<uint16_t *>(y)[m * N + n] = (uint16_t)h;
+        }
       }
     }
   };
@@ -472,7 +485,9 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
     }
   };
 
-  float acc = 0.f;
+  float acc[MR], part[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
   if constexpr (SX > 0) {
     // slot and slice of every step known at compile time: unroll lcm(2, SX)
     constexpr int U = SX == 3 ? 6 : (SX == 1 ? 2 : SX);
@@ -483,11 +498,21 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
         if (t >= T) break;
         const int j = u & 1, s = u % SX;
         issue((t + 1) / SX, (u + 1) % SX, t + 1 < T, j ^ 1);
+        // keep the item's loads together, ahead of the decode
+        __builtin_amdgcn_sched_barrier(0);
         const float ahat = item_scale(sq[j], sa[j]);
-        acc = fmaf(ahat, decode(w[j], xr[s]), acc);
+        uint4v xq[MR][4];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xq[m][q] = xr[m][s][q];
+        decode(w[j], xq, part);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = fmaf(ahat, part[m], acc[m]);
         if (s == SX - 1) {
           finish_row(t / SX, acc);
-          acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < MR; ++m) acc[m] = 0.f;
         }
       }
     }
@@ -504,27 +529,35 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
         const int64_t t = t0 + j;
         if (t >= T) break;
         issue(rn, sn, t + 1 < T, j ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
         if (++sn == S) {
           sn = 0;
           ++rn;
         }
-        uint4v xq[4];
-        if constexpr (XLDS) {
+        uint4v xq[MR][4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xq[q] = xlv[sd * 256 + q * 64 + lane];
-        } else {
-          // a lane past the row's last piece multiplies its (zero) codes by
-          // zero activations, so it adds nothing
-          const int64_t pc = (int64_t)sd * 64 + lane;
-          const uint4v *xp = reinterpret_cast<const uint4v *>(x + ((pc < pieces ? pc : 0) << 5));
+        for (int m = 0; m < MR; ++m) {
+          if constexpr (XLDS) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xq[q] = pc < pieces ? xp[q] : uint4v{0, 0, 0, 0};
+            for (int q = 0; q < 4; ++q) xq[m][q] = xlv[m * rch + sd * 256 + q * 64 + lane];
+          } else {
+            // a lane past the row's last piece multiplies its (zero) codes by
+            // zero activations, so it adds nothing
+            const int64_t pc = (int64_t)sd * 64 + lane;
+            const uint4v *xp =
+                reinterpret_cast<const uint4v *>(x + m * K + ((pc < pieces ? pc : 0) << 5));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xq[m][q] = pc < pieces ? xp[q] : uint4v{0, 0, 0, 0};
+          }
         }
         const float ahat = item_scale(sq[j], sa[j]);
-        acc = fmaf(ahat, decode(w[j], xq), acc);
+        decode(w[j], xq, part);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = fmaf(ahat, part[m], acc[m]);
         if (sd == S - 1) {
           finish_row(rd, acc);
-          acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < MR; ++m) acc[m] = 0.f;
         }
         if (++sd == S) {
           sd = 0;
@@ -727,7 +760,7 @@ static hipError_t launch_lut_m(const void *x, int64_t N, int64_t K, const uint8_
   return hipGetLastError();
 }
 
-template <int XDT>
+template <int XDT, int MR>
 static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *packed,
                             const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
                             const void *bias, hipStream_t st) {
@@ -738,47 +771,50 @@ static hipError_t launch_m1(const void *x, int64_t N, int64_t K, const uint8_t *
   const int rpw = (int)(N / total_waves), rem = (int)(N % total_waves);
   const uint16_t *xh = static_cast<const uint16_t *>(x);
   const Table16 table = host_table16(qt, XDT);
-  // x staged in LDS as K / 8 chunks of 16 bytes, XC per thread
-  // (whole slices of 2048 values; the tail of the last one is zero-filled)
+  // the MR activation rows staged in LDS as whole slices of 16-byte chunks
+  // (the tail of the last one zero-filled), XC chunks per thread
   const int64_t slices = (K + 2047) / 2048;
-  const int64_t need = (slices * 256 + kM1Threads - 1) / kM1Threads;
-  const int xc =
-      slices * 4096 > kM1XLdsBytes ? 0 : (need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 6);
-  // slices per row held in registers: all of them, for 1 to 4 slices
-  const int sx = (xc > 0 && slices <= 4) ? (int)slices : 0;
+  const int64_t need = (MR * slices * 256 + kM1Threads - 1) / kM1Threads;
+  const int xc = MR * slices * 4096 > kM1XLdsBytes
+                     ? 0
+                     : (need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 6);
+  // slices per row held in registers: all of them, up to 4 slice-rows
+  const int sx = (xc > 0 && MR * slices <= 4) ? (int)slices : 0;
   // one double-quant group per item: whole slices, and a slice's blocks
   // (2048 / blocksize, at least one) within a group
   const int64_t slice_blocks = log2bs >= 11 ? 1 : (int64_t)1 << (11 - log2bs);
   const bool ug = dq && K % 2048 == 0 && slice_blocks <= ((int64_t)1 << sc.log2bs2);
-#define QMV_M1(DQV, XCV, SV)                                                                   \
-  if (ug)                                                                                      \
-    hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, SV, DQV>), dim3((unsigned)grid),   \
-                       dim3(kM1Threads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt,  \
-                       rpw, rem, bias);                                                        \
-  else                                                                                         \
-  hipLaunchKernelGGL((gemv_4bit_m1_kernel<XDT, DQV, XCV, SV, false>), dim3((unsigned)grid),   \
-                     dim3(kM1Threads), 0, st, xh, N, K, packed, sc, log2bs, table, y, ydt, rpw, \
-                     rem, bias)
-#define QMV_M1X(DQV)                                   \
-  switch (sx) {                                        \
-    case 1: QMV_M1(DQV, 1, 1); break;                  \
-    case 2: QMV_M1(DQV, 1, 2); break;                  \
-    case 3: QMV_M1(DQV, 1, 3); break;                  \
-    case 4: QMV_M1(DQV, 1, 4); break;                  \
-    default:                                           \
-      switch (xc) {                                    \
-        case 0: QMV_M1(DQV, 0, 0); break;              \
-        case 1: QMV_M1(DQV, 1, 0); break;              \
-        case 2: QMV_M1(DQV, 2, 0); break;              \
-        case 4: QMV_M1(DQV, 4, 0); break;              \
-        default: QMV_M1(DQV, 6, 0); break;             \
-      }                                                \
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kM1Threads), 0, st, xh, N, K, packed, sc,
+                       log2bs, table, y, ydt, rpw, rem, bias);
+  };
+#define QMV_M1(DQV, XCV, SV)                                               \
+  if (DQV && ug) go(gemv_4bit_m1_kernel<XDT, DQV, XCV, SV, DQV, MR>);      \
+  else go(gemv_4bit_m1_kernel<XDT, DQV, XCV, SV, false, MR>)
+#define QMV_M1X(DQV)                                                       \
+  if (sx == 1) { QMV_M1(DQV, 1, 1); }                                      \
+  else if constexpr (MR <= 2) {                                            \
+    if (sx == 2) { QMV_M1(DQV, 1, 2); }                                    \
+    else if constexpr (MR == 1) {                                          \
+      if (sx == 3) { QMV_M1(DQV, 1, 3); }                                  \
+      else if (sx == 4) { QMV_M1(DQV, 1, 4); }                             \
+      else QMV_M1XC(DQV);                                                  \
+    } else QMV_M1XC(DQV);                                                  \
+  } else QMV_M1XC(DQV)
+#define QMV_M1XC(DQV)                                                      \
+  switch (xc) {                                                            \
+    case 0: QMV_M1(DQV, 0, 0); break;                                      \
+    case 1: QMV_M1(DQV, 1, 0); break;                                      \
+    case 2: QMV_M1(DQV, 2, 0); break;                                      \
+    case 4: QMV_M1(DQV, 4, 0); break;                                      \
+    default: QMV_M1(DQV, 6, 0); break;                                     \
   }
   if (dq) {
     QMV_M1X(true);
   } else {
     QMV_M1X(false);
   }
+#undef QMV_M1XC
 #undef QMV_M1X
 #undef QMV_M1
   return hipGetLastError();
@@ -788,7 +824,16 @@ template <int XDT>
 static hipError_t launch_lut(const void *x, int M, int64_t N, int64_t K, const uint8_t *packed,
                              const Scales &sc, bool dq, int log2bs, int qt, void *y, int ydt,
                              const void *bias, hipStream_t st) {
-  if (M == 1) return launch_m1<XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
+  // 1 to 4 rows: the item-pipelined kernel, while the activation rows fit
+  // in its LDS copy (longer rows of 2 to 4 activation rows take the table
+  // kernel below, which re-reads them per slice from the cache)
+  const int64_t slices = (K + 2047) / 2048;
+  if (M == 1) return launch_m1<XDT, 1>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
+  if (M <= 4 && M * slices * 4096 <= kM1XLdsBytes) {
+    if (M == 2) return launch_m1<XDT, 2>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
+    if (M == 3) return launch_m1<XDT, 3>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
+    return launch_m1<XDT, 4>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
+  }
   switch (M) {
 #define QMV_C(MV) case MV: return launch_lut_m<MV, XDT>(x, N, K, packed, sc, dq, log2bs, qt, y, ydt, bias, st);
     QMV_C(1) QMV_C(2) QMV_C(3) QMV_C(4) QMV_C(5) QMV_C(6) QMV_C(7)

@@ -1,8 +1,9 @@
-"""GPU parity of the M = 1 gemv kernel on every way it can be launched:
-activations held in registers for 1, 2, 3 or 4 slices of 2048 weights per
-row, read per slice from the staged LDS copy (5 to 22 slices), or read from
-global memory (longer rows); partial last slices; more rows than waves (some
-waves carry one extra row) and fewer rows than waves (some carry none).
+"""GPU parity of the gemv kernel for 1 to 4 activation rows (the decode step
+and small batches) on every way it can be launched: activations held in
+registers (up to 4 slices of 2048 weights per row, over all rows), read per
+slice from the staged LDS copy, or read from global memory (longer rows);
+partial last slices; more rows than waves (some waves carry one extra row)
+and fewer rows than waves (some carry none).
 Reference: the CPU oracle's dequantize + float64 matmul.  Tolerance: the
 bf16 activations and the bf16-rounded code table give up to ~1e-2 relative
 L2 for fp32 outputs; bf16 outputs 2e-2."""
@@ -43,7 +44,6 @@ CASES = [
 def test_gemv_m1_paths(N, K, bs, dq, qt):
     seed = N * 7 + K + bs + dq
     W = synth.gaussian((N, K), 0.02, seed, "bf16")
-    x = synth.gaussian((1, K), 1.0, seed + 1, "bf16")
     p_ref, absmax = O.quantize_4bit(f64(W), bs, qt)
     if dq:
         q, a2, off = O.double_quant(absmax, 256)
@@ -52,13 +52,15 @@ def test_gemv_m1_paths(N, K, bs, dq, qt):
         ahat = absmax
     packed, st = qmv.quantize_4bit(W.cuda(), bs, qt, double_quant=dq)
     assert np.array_equal(packed.cpu().numpy(), p_ref)
-    ref = O.matmul_4bit(f64(x), p_ref, ahat, N, K, bs, qt)
-    yf = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=torch.float32)
-    assert yf.shape == (1, N)
-    assert np.all(np.isfinite(f64(yf)))
-    assert rel_l2(f64(yf), ref) <= 1e-2
-    yb = qmv.gemv_4bit(x.cuda(), packed, st)
-    assert rel_l2(f64(yb), ref) <= 2e-2
+    for M in (1, 2, 3, 4):
+        xm = synth.gaussian((M, K), 1.0, seed + 1 + M, "bf16")
+        ref = O.matmul_4bit(f64(xm), p_ref, ahat, N, K, bs, qt)
+        yf = qmv.gemv_4bit(xm.cuda(), packed, st, out_dtype=torch.float32)
+        assert yf.shape == (M, N)
+        assert np.all(np.isfinite(f64(yf)))
+        assert rel_l2(f64(yf), ref) <= 1e-2, M
+        yb = qmv.gemv_4bit(xm.cuda(), packed, st)
+        assert rel_l2(f64(yb), ref) <= 2e-2, M
 
 
 def test_gemv_m1_repeatable():
