@@ -145,6 +145,57 @@ def cpu_baseline(W_cpu, x_cpu, budget_s=15.0, rows=256):
 COPY_BYTES = 1 << 30
 
 
+def measured_ceilings(torch, dev, reps=20):
+    """Streaming ceilings of this GPU, to read the kernels' GB/s against: a
+    plain 128-bit read of 1 GiB (the library's stream_read probe) and torch's
+    device copy of 1 GiB (bytes read + written).  Event-timed on torch's
+    current stream, the probe's launch stream, after two warm-up passes."""
+    from quantized_matvec_amd import qmv
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, fn, nbytes in (("read_gbs", lambda: qmv.stream_read(src, sink), COPY_BYTES),
+                             ("copy_gbs", lambda: dst.copy_(src), 2 * COPY_BYTES)):
+        for _ in range(2):
+            fn()
+        st = torch.cuda.current_stream(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        b.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        out[name] = round(nbytes / us / 1e3, 1)
+    del src, dst
+    out["method"] = ("stream_read probe over 1 GiB (128-bit loads, grid-stride) and torch copy_ of 1 GiB "
+                     "(bytes read + written), event-timed")
+    return out
+
+
+def host_info():
+    """The host side of the cpu_baseline: CPU model, usable and total cores,
+    numpy's BLAS thread pools."""
+    import os
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": d.get("internal_api"), "threads": d.get("num_threads")} for d in threadpool_info()]
+    except Exception:  # noqa: BLE001 - informational only
+        blas = []
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_count": os.cpu_count(), "blas_pools": blas}
+
+
 def counters_run(name, fns, n_copies, dev, torch):
     """A short program for rocprofv3 counter passes: a plain 1 GiB device copy
     (its FETCH_SIZE / WRITE_SIZE per byte calibrate the counters), then ten
@@ -344,6 +395,7 @@ def main():
     gemv_us = kern["gemv_4bit"]
     gemv_gbs = ab["gemv_4bit"] / gemv_us / 1e3
     traffic = measured_traffic()
+    ceil = measured_ceilings(torch, dev)
     out = {
         "metric": METRIC,
         "value": round(gemv_gbs, 1),
@@ -365,12 +417,18 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "gemv_4bit",
-                     "algorithmic_bytes_per_launch": ab["gemv_4bit"], "avg_launch_us": round(gemv_us, 3)},
+                     "algorithmic_bytes_per_launch": ab["gemv_4bit"], "avg_launch_us": round(gemv_us, 3),
+                     "frac_of_measured_read": round(gemv_gbs / ceil["read_gbs"], 4)},
+        "ceilings": ceil,
+        "env": {"torch": torch.__version__, "hip": torch.version.hip,
+                "device": torch.cuda.get_device_name(dev),
+                "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
         "kernels": rep,
         "step_wall_ms": round(wall_step_ms, 4),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W_cpu, x_cpu)
+        out["cpu_baseline"]["host"] = host_info()
     print(json.dumps(out), flush=True)
 
 

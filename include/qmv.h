@@ -225,6 +225,19 @@ int qmv_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D, cons
                        const qmv_absmax *scales, int32_t blocksize, qmv_quant_type quant_type,
                        void *out, qmv_dtype out_dtype, void *stream);
 
+/*
+ * stream_read: a measurement probe, not a step of the method.  Reads every
+ * byte of p once with 128-bit loads (a grid-stride pass over the whole
+ * buffer) and XORs all of its 32-bit words into *sink, so the reads cannot
+ * be elided; timing it over a buffer much larger than the caches gives the
+ * streaming-read ceiling that the bandwidth-bound kernels are compared with.
+ *   p     device, 16-byte aligned (QMV_ERR_ALIGNMENT), bytes > 0 and a
+ *         multiple of 16 (QMV_ERR_INVALID_ARG)
+ *   sink  device uint32, 4-byte aligned; XORed into, not cleared: the caller
+ *         zeroes it to read the checksum.  Concurrent calls on one sink race.
+ */
+int qmv_stream_read(const void *p, int64_t bytes, uint32_t *sink, void *stream);
+
 /* Host-side: the 16 fp32 code values the kernels use, by code. */
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]);
 

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmv.so")
 SOURCES = ["qmv_api.hip", "qmv_codec.hip", "qmv_blockwise.hip", "qmv_embedding.hip", "qmv_gemv.hip",
-           "qmv_gemm.hip"]
+           "qmv_gemm.hip", "qmv_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

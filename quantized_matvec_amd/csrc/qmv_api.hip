@@ -11,6 +11,11 @@
 #include "qmv.h"
 #include "qmv_launch.hpp"
 
+namespace qmv {
+// the streaming-read probe (qmv_probe.hip)
+hipError_t launch_stream_read(const void *p, int64_t bytes, uint32_t *sink, hipStream_t st);
+}  // namespace qmv
+
 using namespace qmv;
 
 namespace {
@@ -310,6 +315,12 @@ int qmv_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D, cons
     return QMV_ERR_ALIGNMENT;
   return launch_status(launch_embedding_4bit(idx, T, V, D, packed, sc, dq, log2_exact(blocksize),
                                              quant_type, out, out_dtype, (hipStream_t)stream));
+}
+
+int qmv_stream_read(const void *p, int64_t bytes, uint32_t *sink, void *stream) {
+  if (!p || !sink || bytes <= 0 || bytes % 16 != 0) return QMV_ERR_INVALID_ARG;
+  if (!aligned16(p) || reinterpret_cast<uintptr_t>(sink) % 4 != 0) return QMV_ERR_ALIGNMENT;
+  return launch_status(launch_stream_read(p, bytes, sink, (hipStream_t)stream));
 }
 
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]) {

@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_embedding_4bit": (ctypes.c_int, [vp, i64, i64, i64, vp, ap, i32, ctypes.c_int, vp,
                                               ctypes.c_int, vp]),
+        "qmv_stream_read": (ctypes.c_int, [vp, i64, vp, vp]),
         "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
         "qmv_default_code2": (ctypes.c_int, [vp]),
         "qmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -368,3 +369,18 @@ def default_code2() -> list:
     buf = (ctypes.c_float * 256)()
     _check(lib().qmv_default_code2(ctypes.cast(buf, ctypes.c_void_p)), "default_code2")
     return list(buf)
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement probe (qmv_stream_read): reads every byte of the contiguous
+    device tensor `buf` once with 128-bit loads and XORs its 32-bit words
+    into `sink` (a one-element int32 device tensor, zeroed here when not
+    given).  Returns the sink; nothing synchronizes."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("stream_read: buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(lib().qmv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)),
+           "stream_read")
+    return sink

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(qmvlib, n), n
 
@@ -182,3 +182,13 @@ def test_embedding_preconditions(qmvlib):
     assert f(P, 4, 10, 64, P, None, 64, NF4, P2, BF16, None) == INVALID
     assert f(P + 4, 4, 10, 64, P, r, 64, NF4, P2, BF16, None) == ALIGN
     assert f(P, 4, 10, 64, P, r, 64, NF4, MIS, BF16, None) == ALIGN
+
+
+def test_stream_read_preconditions(qmvlib):
+    f = qmvlib.qmv_stream_read
+    assert f(None, 1024, P2, None) == INVALID
+    assert f(P, 1024, None, None) == INVALID
+    assert f(P, 0, P2, None) == INVALID
+    assert f(P, 1000, P2, None) == INVALID          # not a multiple of 16
+    assert f(P + 8, 1024, P2, None) == ALIGN
+    assert f(P, 1024, P2 + 2, None) == ALIGN
