@@ -845,9 +845,11 @@ static hipError_t launch_lut(const void *x, int M, int64_t N, int64_t K, const u
 hipError_t launch_gemv_4bit(const void *x, int x_dtype, int M, int64_t N, int64_t K,
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,
                             void *y, int y_dtype, const void *bias, hipStream_t st) {
-  // 4 to 8 rows of 16-bit activations: the MFMA kernel of gemm_4bit (the
+  // 4 to 8 rows of 16-bit activations, or 2 to 3 rows too long for the
+  // item-pipelined kernel's LDS copy: the MFMA kernel of gemm_4bit (the
   // table kernel's dot products grow with M, the MFMA's do not)
-  if (x_dtype != kF32 && M >= 4 && gemm_narrow_eligible(M, K, log2bs))
+  const bool rows_fit = (int64_t)M * ((K + 2047) / 2048) * 4096 <= kM1XLdsBytes;
+  if (x_dtype != kF32 && (M >= 4 || (M >= 2 && !rows_fit)) && gemm_narrow_eligible(M, K, log2bs))
     return launch_gemm_4bit(x, x_dtype, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, bias, st);
   if (x_dtype == kBF16) return launch_lut<kBF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, bias, st);
   if (x_dtype == kF16) return launch_lut<kF16>(x, M, N, K, packed, sc, dq, log2bs, qt, y, y_dtype, bias, st);
