@@ -494,10 +494,8 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(const float *__restrict__ a
     l = min(l, li);
     stage[i * (kFanIn + 1) + tid] = (double)v[i];
   }
-  for (int o = 1; o < 64; o <<= 1) {
-    h = max(h, __shfl_xor(h, o));
-    l = min(l, __shfl_xor(l, o));
-  }
+  h = wave_max_i32(h);
+  l = wave_min_i32(l);
   if (lane == 0) {
     wh[wave] = h;
     wl[wave] = l;
@@ -512,8 +510,7 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(const float *__restrict__ a
     for (int r = 0; r < 4; ++r) {
       const int run = 4 * wave + r;
       const double *row = stage + run * (kFanIn + 1) + 4 * lane;
-      double t = (row[0] + row[1]) + (row[2] + row[3]);
-      for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+      const double t = wave_sum_f64((row[0] + row[1]) + (row[2] + row[3]));
       if (lane == 0 && run0 + run < nout) levels[run0 + run] = t;
     }
   } else if (tid < kSumRuns && run0 + tid < nout) {
@@ -580,10 +577,8 @@ __device__ __forceinline__ float fused_offset(const double *__restrict__ levels,
     h = max(h, st.x);
     l = min(l, st.y);
   }
-  for (int o = 1; o < 64; o <<= 1) {
-    h = max(h, __shfl_xor(h, o));
-    l = min(l, __shfl_xor(l, o));
-  }
+  h = wave_max_i32(h);
+  l = wave_min_i32(l);
   int *ri = reinterpret_cast<int *>(red);
   if (lane == 0) {
     ri[2 * wave] = h;
@@ -601,7 +596,7 @@ __device__ __forceinline__ float fused_offset(const double *__restrict__ levels,
     double t = 0.0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) t += v[k];
-    for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+    t = wave_sum_f64(t);
     if (lane == 0) red[wave] = t;
     __syncthreads();
     total = (red[0] + red[1]) + (red[2] + red[3]);
@@ -755,9 +750,17 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
 #pragma unroll
       for (int e = 0; e < E; ++e) code[e] = lo[e];
     }
+    if (i0 + E <= n) {  // whole: E codes in E / 4 word stores (q + i0 is E-byte aligned)
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (i0 + e < n) q[i0 + e] = (uint8_t)code[e];
+      for (int w = 0; w < E / 4; ++w)
+        reinterpret_cast<uint32_t *>(q + i0)[w] =
+            (uint32_t)code[4 * w] | ((uint32_t)code[4 * w + 1] << 8) |
+            ((uint32_t)code[4 * w + 2] << 16) | ((uint32_t)code[4 * w + 3] << 24);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (i0 + e < n) q[i0 + e] = (uint8_t)code[e];
+    }
   }
 }
 

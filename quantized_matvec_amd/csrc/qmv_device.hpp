@@ -144,6 +144,52 @@ __device__ __forceinline__ float group_max(float m, int G) {
   return __uint_as_float(u);
 }
 
+// Whole-wave reductions with DPP: row moves inside rows of 16 lanes, then
+// row broadcasts (lane 15 into row 1 and 3, lane 31 into rows 2 and 3), so
+// lane 63 ends with the total, which is read back as a uniform value.  Lanes
+// a move does not write keep `fill` (the operation's identity).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_fill(int x, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+  constexpr int lo = -2147483647 - 1;
+  v = max(v, dpp_fill<0xb1, 0xf>(v, lo));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_fill<0x4e, 0xf>(v, lo));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_fill<0x141, 0xf>(v, lo));  // row_half_mirror
+  v = max(v, dpp_fill<0x140, 0xf>(v, lo));  // row_mirror
+  v = max(v, dpp_fill<0x142, 0xa>(v, lo));  // row_bcast:15
+  v = max(v, dpp_fill<0x143, 0xc>(v, lo));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) { return -wave_max_i32(-v); }
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {  // lanes not written read +0
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)dpp_fill<CTRL, ROW_MASK>((int)(uint32_t)u, 0);
+  const uint32_t hi = (uint32_t)dpp_fill<CTRL, ROW_MASK>((int)(uint32_t)(u >> 32), 0);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum of a double over the wave.  The additions happen in a fixed tree, so
+// it is the exact sum only when every partial sum is exact (the callers
+// check that first).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xb1, 0xf>(v);
+  v += dpp_f64<0x4e, 0xf>(v);
+  v += dpp_f64<0x141, 0xf>(v);
+  v += dpp_f64<0x140, 0xf>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  v += dpp_f64<0x143, 0xc>(v);
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v_t;
