@@ -311,6 +311,7 @@ static hipError_t launch_quantize_t(const void *W, int64_t numel, int log2bs, co
 // share a bin and the midpoint nearest to a bin edge is as far from it as
 // possible (at least 0.02 bin); J(b) counts the midpoints below bin b.
 // Bins of n in [-1, 1] are 1 .. 2 S + 2 < kQBins.
+static_assert(2 * 30 + 2 < kQBins, "the bins of n in [-1, 1] lie below kQBins for every S tried");
 static bool bin_geometry(const Midpoints4 &m, int nt, QuantArgs &qa) {
   double best = 0.0;
   for (int S = 14; S <= 30; ++S) {
