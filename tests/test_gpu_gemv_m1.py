@@ -15,6 +15,7 @@ import oracle as O
 from quantized_matvec_amd import qmv, synth
 
 pytestmark = pytest.mark.gpu
+TDT = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
 
 def f64(t):
@@ -72,3 +73,28 @@ def test_gemv_m1_repeatable():
     y1 = qmv.gemv_4bit(x, packed, st, out_dtype=torch.float32)
     y2 = qmv.gemv_4bit(x, packed, st, out_dtype=torch.float32)
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("M,odt", [(1, "fp32"), (3, "bf16")])
+def test_gemv_m1_long_runs_with_bias(M, odt):
+    """More than 64 rows per wave (64 * 4096 + 100 rows): the bias of rows past
+    a run's 64th is read per row instead of from the read-ahead copy (fp32
+    and 16-bit bias, which take different loads)."""
+    N, K, bs = 64 * 4096 + 100, 64, 64
+    W = synth.gaussian((N, K), 0.02, 91, "bf16")
+    x = synth.gaussian((M, K), 1.0, 92, "bf16")
+    bias = synth.gaussian((N,), 0.1, 93, odt)
+    p_ref, absmax = O.quantize_4bit(f64(W), bs, "nf4")
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "nf4")
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    ref = O.matmul_4bit(f64(x), p_ref, absmax, N, K, bs, "nf4") + f64(bias)[None, :]
+    y = qmv.gemv_4bit(x.cuda(), packed, st, out_dtype=TDT[odt], bias=bias.cuda())
+    tol = 1e-2 if odt == "fp32" else 2e-2
+    assert rel_l2(f64(y), ref) <= tol
+    # the rows past each run's 64th, checked on their own
+    runs = 4096
+    rpw, rem = N // runs, N % runs
+    starts = np.array([r * rpw + min(r, rem) for r in range(runs)])
+    late = (starts[:, None] + np.arange(64, rpw + 1)[None, :]).reshape(-1)
+    late = late[late < N]
+    assert rel_l2(f64(y)[:, late], ref[:, late]) <= tol
