@@ -317,7 +317,7 @@ def main():
         dq_out = [(torch.empty_like(st0.absmax_q), torch.empty_like(st0.absmax2),
                    torch.empty_like(st0.offset), torch.empty_like(st0.code2)) for _ in range(n_w)]
         nbk = N * K // BS
-        ws = torch.zeros(L.qmv_double_quant_workspace(nbk), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(L.qmv_double_quant_workspace(nbk, 256), dtype=torch.uint8, device=dev)
 
         def run_dq(i):
             q, a2, off, c2 = dq_out[i % n_w]

@@ -87,13 +87,20 @@ typedef struct {
 int qmv_quantize_4bit(const void *W, qmv_dtype w_dtype, int64_t numel, int32_t blocksize,
                       qmv_quant_type quant_type, uint8_t *packed, float *absmax, void *stream);
 
-/* Bytes of device workspace qmv_double_quant needs for ``nblocks`` scales
- * (the partial sums of the mean and the exponent bounds of their inputs). */
-size_t qmv_double_quant_workspace(int64_t nblocks);
+/* Bytes of device workspace qmv_double_quant needs for ``nblocks`` scales in
+ * groups of ``blocksize2`` (the partial sums of the mean and the exponent
+ * bounds of their inputs; the mean's tree does not depend on blocksize2).
+ * Returns 0 when nblocks <= 0 or blocksize2 is not a power of two in
+ * [32, 4096]. */
+size_t qmv_double_quant_workspace(int64_t nblocks, int32_t blocksize2);
 
 /*
  * double_quant ("mps-bitsandbytes 0.4.7", "Functional API", Double
  * Quantization: double_quant(absmax, double_quant_block=256)).
+ * The second-level table comes in on the host and goes out on the device:
+ * the host checks that its midpoints are exact before anything is launched
+ * (the encoder's exactness depends on it), and the device copy is what every
+ * decoding call (qmv_absmax.code2) reads.
  *   absmax      [nblocks] device fp32 scales (non-negative)
  *   blocksize2  power of two in [32, 4096] (256 in the reference usage)
  *   code2_host  [256] HOST fp32 table, strictly increasing, or NULL for the
@@ -106,9 +113,10 @@ size_t qmv_double_quant_workspace(int64_t nblocks);
  *   offset      [1] device out: fp32(S / nblocks), S the float64 sum of the
  *               scales taken in a fixed tree (sequential runs of 256, repeated)
  *   code2_out   [256] device out: the table used, for the decode side
- *   workspace   device scratch of at least qmv_double_quant_workspace(nblocks)
- *               bytes (any contents); calls that share a workspace must not
- *               overlap.
+ *   workspace   device scratch of at least
+ *               qmv_double_quant_workspace(nblocks, blocksize2) bytes (any
+ *               contents); calls that share a workspace must not overlap.
+ *               QMV_ERR_WORKSPACE when it is NULL or smaller.
  */
 int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
                      const float *code2_host, uint8_t *absmax_q, float *absmax2, float *offset,
@@ -225,24 +233,22 @@ int qmv_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D, cons
                        const qmv_absmax *scales, int32_t blocksize, qmv_quant_type quant_type,
                        void *out, qmv_dtype out_dtype, void *stream);
 
-/*
- * stream_read: a measurement probe, not a step of the method.  Reads every
- * byte of p once with 128-bit loads (a grid-stride pass over the whole
- * buffer) and XORs all of its 32-bit words into *sink, so the reads cannot
- * be elided; timing it over a buffer much larger than the caches gives the
- * streaming-read ceiling that the bandwidth-bound kernels are compared with.
- *   p     device, 16-byte aligned (QMV_ERR_ALIGNMENT), bytes > 0 and a
- *         multiple of 16 (QMV_ERR_INVALID_ARG)
- *   sink  device uint32, 4-byte aligned; XORed into, not cleared: the caller
- *         zeroes it to read the checksum.  Concurrent calls on one sink race.
- */
-int qmv_stream_read(const void *p, int64_t bytes, uint32_t *sink, void *stream);
-
 /* Host-side: the 16 fp32 code values the kernels use, by code. */
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]);
 
 /* Host-side: the default 256-entry second-level table, (k - 127) / 127 in fp32. */
 int qmv_default_code2(float out256[256]);
+
+/* Host-side: the signed dynamic-tree 8-bit table, ascending, for
+ * qmv_quantize_blockwise / qmv_dequantize_blockwise and double quantization
+ * ("Feat/mps gemm 4bit bf16", "What runs natively now": the 8-bit blockwise
+ * codec; the pages name no table, so this is the reading taken): after the
+ * sign bit, a run of e zero bits (e = 0..6) is a decimal exponent, then a one
+ * bit, then 6 - e fraction bits j picking the centre of bin j of [0.1, 1] cut
+ * into 2^(6-e) bins.  Each value 10^-e (0.1 + 0.9 (j + 1/2) / 2^(6-e)) is
+ * rounded once, exactly, to fp32; with their negatives, 0 and 1 that is 256
+ * strictly increasing values. */
+int qmv_dynamic_code2(float out256[256]);
 
 /* Host-side: a static, human-readable name of a qmv_status value. */
 const char *qmv_status_string(int status);

@@ -215,8 +215,14 @@ def nearest_codes_threshold(x, a, table) -> np.ndarray:
     return code_of[rank]
 
 
-def nearest_codes(x, a, table) -> np.ndarray:
-    """Exact nearest code (R3).  Both formulations run and must agree."""
+def nearest_codes(x, a, table, forms: str = "both") -> np.ndarray:
+    """Exact nearest code (R3).  By default both formulations run and must
+    agree; ``forms="threshold"`` runs the threshold form alone (the same
+    decisions, pinned against the literal form and exact-rational brute force
+    by the tests; used for whole tensors at full size, where 16 or 256
+    distances per element take too long)."""
+    if forms == "threshold":
+        return nearest_codes_threshold(x, a, table)
     lit = nearest_codes_literal(x, a, table)
     thr = nearest_codes_threshold(x, a, table)
     bad = np.flatnonzero(lit != thr)
@@ -246,21 +252,23 @@ def unpack_nibbles(packed, numel: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # quantize_4bit
 # --------------------------------------------------------------------------
-def quantize_4bit(w, blocksize: int = 64, quant_type: str = "nf4"):
+def quantize_4bit(w, blocksize: int = 64, quant_type: str = "nf4", forms: str = "both"):
     """Returns (packed uint8 [ceil(numel/2)], absmax fp32 [ceil(numel/bs)]).
 
     "Functional API" (4-bit): per-block absmax, nearest NF4/FP4 code, two codes
-    per byte; "What runs natively now": quantize_4bit is one of the ops."""
+    per byte; "What runs natively now": quantize_4bit is one of the ops.
+    ``forms`` as for nearest_codes."""
     x = np.asarray(w, dtype=np.float64).ravel()
     table = code_table(quant_type)
     absmax = block_absmax(x, blocksize)
     codes = np.empty(x.size, dtype=np.uint8)
-    step = max(blocksize, (_CHUNK // blocksize) * blocksize)
+    chunk = _CHUNK if forms == "both" else _CHUNK * 16
+    step = max(blocksize, (chunk // blocksize) * blocksize)
     for s in range(0, x.size, step):
         xs = x[s:s + step]
         a = np.repeat(absmax[s // blocksize: s // blocksize + -(-xs.size // blocksize)],
                       blocksize)[: xs.size]
-        codes[s:s + step] = nearest_codes(xs, a, table)
+        codes[s:s + step] = nearest_codes(xs, a, table, forms)
     a32 = absmax.astype(np.float32)
     assert np.array_equal(a32.astype(np.float64), absmax)   # absmax is exact in fp32
     return pack_nibbles(codes), a32
@@ -286,7 +294,7 @@ def mean_fixed_tree(absmax) -> np.float32:
     return np.float32(level[0] / n)
 
 
-def double_quant(absmax, blocksize2: int = 256, code2=None):
+def double_quant(absmax, blocksize2: int = 256, code2=None, forms: str = "both"):
     """Returns (q uint8 [n], absmax2 fp32 [ceil(n/bs2)], offset fp32).
 
     "Functional API" (Double Quantization): double_quant(absmax,
@@ -298,7 +306,7 @@ def double_quant(absmax, blocksize2: int = 256, code2=None):
     c = (a - offset).astype(np.float32)                  # fp32 subtraction, RN
     s = block_absmax(c.astype(np.float64), blocksize2)   # exact
     s_el = np.repeat(s, blocksize2)[: a.size]
-    q = nearest_codes(c.astype(np.float64), s_el, code2)
+    q = nearest_codes(c.astype(np.float64), s_el, code2, forms)
     return q.astype(np.uint8), s.astype(np.float32), offset
 
 

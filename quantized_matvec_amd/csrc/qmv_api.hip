@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "qmv.h"
+#include "qmv_probe.h"
 #include "qmv_launch.hpp"
 
 namespace qmv {
@@ -129,8 +130,8 @@ int qmv_quantize_4bit(const void *W, qmv_dtype w_dtype, int64_t numel, int32_t b
                                             (hipStream_t)stream));
 }
 
-size_t qmv_double_quant_workspace(int64_t nblocks) {
-  return nblocks > 0 ? double_quant_workspace_bytes(nblocks) : 0;
+size_t qmv_double_quant_workspace(int64_t nblocks, int32_t blocksize2) {
+  return nblocks > 0 && valid_blocksize(blocksize2) ? double_quant_workspace_bytes(nblocks) : 0;
 }
 
 // A second-level table is usable when it is finite and strictly increasing
@@ -333,6 +334,39 @@ int qmv_code_table(qmv_quant_type quant_type, float out16[16]) {
 int qmv_default_code2(float out256[256]) {
   if (!out256) return QMV_ERR_INVALID_ARG;
   for (int k = 0; k < 256; ++k) out256[k] = (float)(k - 127) / 127.0f;  // correctly rounded
+  return QMV_OK;
+}
+
+// Exact round-to-nearest-even of p / q (p, q > 0 integers, p / q in the
+// normal fp32 range) to fp32, in integer arithmetic.
+static float rational_to_f32(uint64_t p, uint64_t q) {
+  int k = 0;  // p / q = m * 2^k with m in [2^23, 2^24)
+  unsigned __int128 num = p, den = q;
+  while (num < (den << 23)) { num <<= 1; --k; }
+  while (num >= (den << 24)) { den <<= 1; ++k; }
+  uint64_t m = (uint64_t)(num / den);
+  const unsigned __int128 rem2 = (num - (unsigned __int128)m * den) * 2;
+  if (rem2 > den || (rem2 == den && (m & 1))) ++m;  // nearest, ties to even
+  return ldexpf((float)m, k);                         // m <= 2^24: exact
+}
+
+int qmv_dynamic_code2(float out256[256]) {
+  if (!out256) return QMV_ERR_INVALID_ARG;
+  // 10^-e (0.1 + 0.9 (j + 1/2) / 2^(6-e)) = (2^(7-e) + 18 j + 9) / (10^(e+1) 2^(7-e))
+  std::vector<float> v = {0.0f, 1.0f};
+  for (int e = 0; e <= 6; ++e) {
+    uint64_t pow10 = 10;
+    for (int i = 0; i < e; ++i) pow10 *= 10;
+    const uint64_t bins = 1ull << (6 - e);
+    for (uint64_t j = 0; j < bins; ++j) {
+      const float f = rational_to_f32(2 * bins + 18 * j + 9, pow10 * 2 * bins);
+      v.push_back(f);
+      v.push_back(-f);
+    }
+  }
+  std::sort(v.begin(), v.end());
+  if (v.size() != 256) return QMV_ERR_INVALID_ARG;
+  for (int k = 0; k < 256; ++k) out256[k] = v[k];
   return QMV_OK;
 }
 

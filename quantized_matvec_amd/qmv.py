@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
     ap = ctypes.POINTER(_Absmax)
     sig = {
         "qmv_quantize_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, ctypes.c_int, vp, vp, vp]),
-        "qmv_double_quant_workspace": (sz, [i64]),
+        "qmv_double_quant_workspace": (sz, [i64, i32]),
         "qmv_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "qmv_dequantize_absmax": (ctypes.c_int, [ap, i64, vp, vp]),
         "qmv_dequantize_4bit": (ctypes.c_int, [vp, ap, i64, i32, ctypes.c_int, vp, ctypes.c_int, vp]),
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "qmv_stream_read": (ctypes.c_int, [vp, i64, vp, vp]),
         "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
         "qmv_default_code2": (ctypes.c_int, [vp]),
+        "qmv_dynamic_code2": (ctypes.c_int, [vp]),
         "qmv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -176,7 +177,7 @@ def _double_quant(absmax: torch.Tensor, blocksize2: int = 256, code2: Optional[l
     a2 = torch.empty(-(-n // blocksize2), dtype=torch.float32, device=dev)
     off = torch.empty(1, dtype=torch.float32, device=dev)
     c2 = torch.empty(256, dtype=torch.float32, device=dev)
-    wsb = lib().qmv_double_quant_workspace(n)
+    wsb = lib().qmv_double_quant_workspace(n, blocksize2)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     host = None
     if code2 is not None:
@@ -202,6 +203,7 @@ def dequantize_absmax(state: QuantState) -> torch.Tensor:
 
 def dequantize_4bit(packed: torch.Tensor, state: QuantState, out: Optional[torch.Tensor] = None,
                     out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    _check_state(packed, state)
     packed = _dev(packed, "packed")
     if out is None:
         out = torch.empty(state.shape, dtype=out_dtype or state.dtype, device=packed.device)
@@ -214,10 +216,42 @@ def dequantize_4bit(packed: torch.Tensor, state: QuantState, out: Optional[torch
     return out
 
 
+def _check_state(packed: torch.Tensor, state: QuantState, device=None) -> None:
+    """Refuses a packed tensor or QuantState whose sizes or devices do not
+    match, before anything reaches a kernel (which would otherwise read past
+    the ends of the buffers)."""
+    if packed.dtype != torch.uint8 or packed.numel() != (state.numel + 1) // 2:
+        raise ValueError(f"packed must hold ceil(numel / 2) = {(state.numel + 1) // 2} uint8 "
+                         f"bytes, got {packed.numel()} of {packed.dtype}")
+    nb = state.nblocks
+    if state.absmax is not None:
+        parts = {"absmax": (state.absmax, nb, torch.float32)}
+        if any(t is not None for t in (state.absmax_q, state.absmax2, state.offset, state.code2)):
+            raise ValueError("a QuantState has either plain or double-quantized scales, not both")
+    else:
+        if any(t is None for t in (state.absmax_q, state.absmax2, state.offset, state.code2)):
+            raise ValueError("double-quantized scales need absmax_q, absmax2, offset and code2")
+        parts = {"absmax_q": (state.absmax_q, nb, torch.uint8),
+                 "absmax2": (state.absmax2, -(-nb // state.blocksize2), torch.float32),
+                 "offset": (state.offset, 1, torch.float32),
+                 "code2": (state.code2, 256, torch.float32)}
+    dev = packed.device if device is None else device
+    for name, (t, n, dt) in parts.items():
+        if t.numel() != n or t.dtype != dt:
+            raise ValueError(f"{name} must hold {n} values of {dt}, got {t.numel()} of {t.dtype}")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the operands on {dev}")
+    if packed.device != dev:
+        raise ValueError(f"packed is on {packed.device}, the operands on {dev}")
+
+
 def _matmul(name, x, packed, state, out, out_dtype, bias):
     if len(state.shape) != 2:
         raise ValueError("the quantized weight must be 2-D [N, K]")
     N, K = state.shape
+    if x.dim() < 1 or x.shape[-1] != K:
+        raise ValueError(f"x must have K = {K} elements in its last dimension, got {tuple(x.shape)}")
+    _check_state(packed, state, x.device)
     packed = _dev(packed, "packed")
     x = _dev(x, "x")
     x2 = x.reshape(-1, K)
@@ -292,20 +326,12 @@ def dequantize_blockwise(q: torch.Tensor, absmax: torch.Tensor, blocksize: int =
 
 
 def dynamic_tree_code() -> list:
-    """A signed dynamic-tree 8-bit table: a decimal exponent e = 0 .. 6 taken
-    by a run of leading zero bits, then 6 - e bits of linear fraction in
-    [0.1, 1] (bin centres), so each value is 10^-e * (0.1 + 0.9 (j + 1/2) /
-    2^(6 - e)); with their negatives, 0 and 1 that is 256 values, sorted."""
-    vals = {0.0, 1.0}
-    for e in range(7):
-        nf = 1 << (6 - e)
-        for j in range(nf):
-            v = float(torch.tensor(10.0 ** -e * (0.1 + 0.9 * (j + 0.5) / nf), dtype=torch.float32))
-            vals.add(v)
-            vals.add(-v)
-    out = sorted(vals)
-    assert len(out) == 256
-    return out
+    """The library's signed dynamic-tree 8-bit table (qmv_dynamic_code2):
+    256 ascending fp32 values, a decimal exponent e = 0 .. 6 taken by a run of
+    leading zero bits, then 6 - e bits of linear fraction in [0.1, 1]."""
+    buf = (ctypes.c_float * 256)()
+    _check(lib().qmv_dynamic_code2(ctypes.cast(buf, ctypes.c_void_p)), "dynamic_code2")
+    return list(buf)
 
 
 def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState,
@@ -315,6 +341,9 @@ def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState
     if len(state.shape) != 2:
         raise ValueError("the quantized weight must be 2-D [N, K]")
     N, K = state.shape
+    if dY.dim() < 1 or dY.shape[-1] != N:
+        raise ValueError(f"dY must have N = {N} elements in its last dimension, got {tuple(dY.shape)}")
+    _check_state(packed, state, dY.device)
     packed = _dev(packed, "packed")
     dY = _dev(dY, "dY")
     g2 = dY.reshape(-1, N)
@@ -338,6 +367,7 @@ def embedding_4bit(idx: torch.Tensor, packed: torch.Tensor, state: QuantState,
     if len(state.shape) != 2:
         raise ValueError("the quantized table must be 2-D [V, D]")
     V, D = state.shape
+    _check_state(packed, state, idx.device)
     packed = _dev(packed, "packed")
     idx = _dev(idx, "idx")
     if idx.dtype in (torch.int32, torch.int16, torch.uint8):

@@ -1,4 +1,4 @@
-"""The C ABI without a GPU: every symbol include/qmv.h declares is exported,
+"""The C ABI without a GPU: every symbol include/*.h declares is exported,
 the host-side tables match the oracle bit for bit, and every precondition
 comes back as its status code before anything is launched.
 
@@ -24,14 +24,17 @@ NF4, FP4 = 0, 1
 
 
 def header_functions():
-    with open(os.path.join(ROOT, "include", "qmv.h")) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            with open(os.path.join(ROOT, "include", h)) as f:
+                names |= set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", f.read()))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
     for n in names:
         assert hasattr(qmvlib, n), n
 
@@ -71,9 +74,12 @@ def test_quantize_preconditions(qmvlib):
 
 def test_double_quant_preconditions(qmvlib):
     f = qmvlib.qmv_double_quant
-    ws = qmvlib.qmv_double_quant_workspace(1000)
+    ws = qmvlib.qmv_double_quant_workspace(1000, 256)
     assert ws == 8 * (4 + 1) + 8  # level sums (4 runs, then 1), one exponent-bound pair
-    assert qmvlib.qmv_double_quant_workspace(0) == 0
+    assert qmvlib.qmv_double_quant_workspace(1000, 32) == ws   # the mean's tree is fixed
+    assert qmvlib.qmv_double_quant_workspace(0, 256) == 0
+    assert qmvlib.qmv_double_quant_workspace(1000, 48) == 0
+    assert qmvlib.qmv_dynamic_code2(None) == INVALID
     args = lambda **k: dict(dict(a=P, n=1000, bs2=256, code=None, q=P, a2=P, off=P, c2o=P, w=P2, wsb=ws), **k)
     call = lambda d: f(d["a"], d["n"], d["bs2"], d["code"], d["q"], d["a2"], d["off"], d["c2o"], d["w"], d["wsb"], None)
     assert call(args(n=0)) == INVALID
@@ -192,3 +198,50 @@ def test_stream_read_preconditions(qmvlib):
     assert f(P, 1000, P2, None) == INVALID          # not a multiple of 16
     assert f(P + 8, 1024, P2, None) == ALIGN
     assert f(P, 1024, P2 + 2, None) == ALIGN
+
+
+# ---------------------------------------------------------------- Python-side refusals
+def _state(N=64, K=128, bs=64, dq=False, nb=None, packed_bytes=None):
+    import torch
+    nb = (N * K) // bs if nb is None else nb
+    packed = torch.zeros((N * K) // 2 if packed_bytes is None else packed_bytes, dtype=torch.uint8)
+    if dq:
+        st = qmv.QuantState((N, K), torch.bfloat16, bs, "nf4", None,
+                            torch.zeros(nb, dtype=torch.uint8), torch.zeros(-(-nb // 256)),
+                            torch.zeros(1), torch.zeros(256), 256)
+    else:
+        st = qmv.QuantState((N, K), torch.bfloat16, bs, "nf4", absmax=torch.zeros(nb))
+    return packed, st
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_binding_refuses_mismatched_state(dq):
+    """Sizes that would make a kernel read past a buffer are refused in
+    Python, before any device call (CPU tensors: the size checks come first)."""
+    import torch
+    x = torch.zeros(1, 128, dtype=torch.bfloat16)
+    packed, st = _state(dq=dq, packed_bytes=100)
+    with pytest.raises(ValueError, match="packed must hold"):
+        qmv.gemv_4bit(x, packed, st)
+    packed, st = _state(dq=dq, nb=100)
+    with pytest.raises(ValueError, match="absmax"):
+        qmv.gemm_4bit(x, packed, st)
+    with pytest.raises(ValueError, match="absmax"):
+        qmv.dequantize_4bit(packed, st)
+    packed, st = _state(dq=dq)
+    with pytest.raises(ValueError, match="last dimension"):
+        qmv.gemv_4bit(torch.zeros(1, 127, dtype=torch.bfloat16), packed, st)
+    with pytest.raises(ValueError, match="last dimension"):
+        qmv.gemm_4bit_backward(torch.zeros(2, 63, dtype=torch.bfloat16), packed, st)
+    if dq:
+        st.code2 = torch.zeros(255)
+        with pytest.raises(ValueError, match="code2"):
+            qmv.gemv_4bit(x, packed, st)
+        st.code2 = torch.zeros(256)
+        st.absmax = torch.zeros(st.nblocks)
+        with pytest.raises(ValueError, match="not both"):
+            qmv.gemv_4bit(x, packed, st)
+    # a well-formed state on the CPU gets as far as the device check
+    packed, st = _state(dq=dq)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qmv.gemv_4bit(x, packed, st)

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import crafted_inputs
 import oracle as O
 from quantized_matvec_amd import qmv
 
@@ -142,6 +143,22 @@ def test_double_quant_mean_wide_exponents(n):
     q, a2, off, c2 = qmv.double_quant(ag, 256)
     torch.cuda.synchronize()
     q_ref, a2_ref, off_ref = O.double_quant(a, 256)
+    assert bits32(off.cpu().numpy())[0] == bits32([off_ref])[0]
+    assert np.array_equal(bits32(a2.cpu().numpy()), bits32(a2_ref))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("which", ["two_level", "three_level"])
+def test_double_quant_mean_crafted_order(which):
+    """Scales built so that every other summation order (flat, pairwise,
+    other fan-ins, a pairwise upper level) rounds the fp32 mean differently
+    from the fixed 256-run tree (the oracle pins assert each difference):
+    the offset must be the tree's, 16384.0 and 64.0."""
+    a = getattr(crafted_inputs, "mean_" + which)()
+    q, a2, off, c2 = qmv.double_quant(torch.from_numpy(a).cuda(), 256)
+    torch.cuda.synchronize()
+    q_ref, a2_ref, off_ref = O.double_quant(a, 256, forms="threshold")
+    assert float(off_ref) == (16384.0 if which == "two_level" else 64.0)
     assert bits32(off.cpu().numpy())[0] == bits32([off_ref])[0]
     assert np.array_equal(bits32(a2.cpu().numpy()), bits32(a2_ref))
     assert np.array_equal(q.cpu().numpy(), q_ref)

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle as O
+from bounds import check_backward, check_matmul
 from quantized_matvec_amd import qmv, synth
 
 pytestmark = pytest.mark.gpu
@@ -47,12 +48,6 @@ def draw(i):
     )
 
 
-def tol(xdt, odt):
-    if odt != "fp32":
-        return 2e-2
-    return {"bf16": 1e-2, "fp16": 2e-3, "fp32": 1e-5}[xdt]
-
-
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_sweep(i):
     c = draw(i)
@@ -73,18 +68,17 @@ def test_sweep(i):
     assert np.array_equal(w.view(np.uint32), w_ref.view(np.uint32)), c
 
     bias = synth.gaussian((N,), 0.1, c["seed"] + 1, c["odt"]).cuda() if c["bias"] else None
-    b64 = f64(bias)[None, :] if bias is not None else 0.0
+    b64 = f64(bias) if bias is not None else None
+    Wh = w_ref.reshape(N, K)
     for M, f in ((c["M_gemv"], qmv.gemv_4bit), (c["M_gemm"], qmv.gemm_4bit)):
         x = synth.gaussian((M, K), 1.0, c["seed"] + 2 + M, c["xdt"])
         y = f(x.cuda(), packed, st, out_dtype=TDT[c["odt"]], bias=bias)
-        ref = O.matmul_4bit(f64(x), p_ref, ahat, N, K, bs, qt) + b64
         assert y.shape == (M, N)
-        assert rel_l2(f64(y), ref) <= tol(c["xdt"], c["odt"]), (c, M, f.__name__)
+        check_matmul(f64(y), f64(x), Wh, c["xdt"], c["odt"], f"{c} M={M} {f.__name__}", bias=b64)
 
     # backward (16-bit dY, N a multiple of 32)
     if c["xdt"] != "fp32" and N % 32 == 0:
         M = c["M_gemm"]
         dY = synth.gaussian((M, N), 1.0, c["seed"] + 3, c["xdt"])
         dX = qmv.gemm_4bit_backward(dY.cuda(), packed, st, out_dtype=TDT[c["odt"]])
-        ref = O.matmul_4bit_backward(f64(dY), p_ref, ahat, N, K, bs, qt)
-        assert rel_l2(f64(dX), ref) <= tol(c["xdt"], c["odt"]), (c, "backward")
+        check_backward(f64(dX), f64(dY), Wh, c["xdt"], c["odt"], f"{c} backward")
