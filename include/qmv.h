@@ -51,7 +51,8 @@ typedef enum {
   QMV_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned */
   QMV_ERR_LAUNCH = -4,      /* the HIP runtime refused a kernel launch */
   QMV_ERR_HIP = -5,         /* another HIP runtime call failed */
-  QMV_ERR_WORKSPACE = -6    /* workspace missing or smaller than qmv_double_quant_workspace() */
+  QMV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than qmv_double_quant_workspace() */
+  QMV_ERR_TOO_LARGE = -7    /* more scales than qmv_double_quant_noalloc's fixed scratch holds */
 } qmv_status;
 
 typedef enum { QMV_NF4 = 0, QMV_FP4 = 1 } qmv_quant_type;
@@ -121,6 +122,22 @@ size_t qmv_double_quant_workspace(int64_t nblocks, int32_t blocksize2);
 int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
                      const float *code2_host, uint8_t *absmax_q, float *absmax2, float *offset,
                      float *code2_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * double_quant without a workspace and without any allocation: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The same operation,
+ * kernels and results as qmv_double_quant; the mean's partial sums go to a
+ * scratch array of 576 KiB that the library holds in each GPU's memory until
+ * the process ends (its address is looked up once per device on the first
+ * call there).  Arguments as for qmv_double_quant, without the workspace.
+ *   nblocks  at most 2^24 (16,777,216 scales), else QMV_ERR_TOO_LARGE
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams or from different threads) race.
+ */
+int qmv_double_quant_noalloc(const float *absmax, int64_t nblocks, int32_t blocksize2,
+                             const float *code2_host, uint8_t *absmax_q, float *absmax2,
+                             float *offset, float *code2_out, void *stream);
 
 /* dequant_absmax ("Functional API": dequant_absmax).  absmax_out [nblocks]
  * device fp32; with plain scales it is a copy. */

@@ -186,6 +186,27 @@ int qmv_double_quant(const float *absmax, int64_t nblocks, int32_t blocksize2,
                                            (hipStream_t)stream));
 }
 
+int qmv_double_quant_noalloc(const float *absmax, int64_t nblocks, int32_t blocksize2,
+                             const float *code2_host, uint8_t *absmax_q, float *absmax2,
+                             float *offset, float *code2_out, void *stream) {
+  if (!absmax || !absmax_q || !absmax2 || !offset || !code2_out || nblocks <= 0)
+    return QMV_ERR_INVALID_ARG;
+  if (!valid_blocksize(blocksize2)) return QMV_ERR_UNSUPPORTED;
+  if (nblocks > kNoAllocMaxBlocks) return QMV_ERR_TOO_LARGE;
+  if (!aligned16(absmax) || !aligned16(absmax_q) || !aligned16(absmax2) || !aligned16(offset) ||
+      !aligned16(code2_out))
+    return QMV_ERR_ALIGNMENT;
+  Code2Table t;
+  bool linear;
+  const int rc = code_table8(code2_host, t, linear);
+  if (rc != QMV_OK) return rc;
+  void *ws = nullptr;  // this device's copy of the library's scratch
+  if (double_quant_scratch(&ws) != hipSuccess || ws == nullptr) return QMV_ERR_HIP;
+  return launch_status(launch_double_quant(absmax, nblocks, log2_exact(blocksize2), t, linear,
+                                           absmax_q, absmax2, offset, code2_out, ws,
+                                           (hipStream_t)stream));
+}
+
 int qmv_quantize_blockwise(const void *A, qmv_dtype a_dtype, int64_t n, int32_t blocksize,
                            const float *code_host, uint8_t *q, float *absmax, void *stream) {
   if (!A || !q || !absmax || n <= 0 || !valid_dtype(a_dtype)) return QMV_ERR_INVALID_ARG;
@@ -379,6 +400,7 @@ const char *qmv_status_string(int status) {
     case QMV_ERR_LAUNCH: return "kernel launch failed";
     case QMV_ERR_HIP: return "HIP runtime error";
     case QMV_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMV_ERR_TOO_LARGE: return "more than 2^24 scales for the fixed scratch of qmv_double_quant_noalloc";
     default: return "unknown status";
   }
 }

@@ -765,7 +765,7 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float *__restrict_
   }
 }
 
-size_t double_quant_workspace_bytes(int64_t nblocks) {
+static constexpr size_t dq_workspace_bytes(int64_t nblocks) {
   size_t total = 0;
   int64_t n = nblocks;
   do {
@@ -774,6 +774,40 @@ size_t double_quant_workspace_bytes(int64_t nblocks) {
   } while (n > 1);
   const int64_t runs = (nblocks + kFanIn - 1) / kFanIn;
   return total + (size_t)((runs + kSumRuns - 1) / kSumRuns) * sizeof(int2);  // + exponent bounds
+}
+
+size_t double_quant_workspace_bytes(int64_t nblocks) { return dq_workspace_bytes(nblocks); }
+
+// The fixed scratch of the allocation-free double quantization: the mean tree
+// and exponent bounds for up to kNoAllocMaxBlocks scales.  One copy per GPU,
+// held until the process ends; every call on that GPU reuses it (the kernels
+// overwrite it before reading it, so it needs no clearing), so calls that
+// overlap on one GPU race.  In host code `scratch` is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = 576 * 1024;
+static_assert(dq_workspace_bytes(kNoAllocMaxBlocks) <= kNoAllocScratchBytes,
+              "scratch too small for kNoAllocMaxBlocks scales");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_ptr[kMaxDevices];
+hipError_t scratch_status[kMaxDevices];
+}  // namespace
+
+hipError_t double_quant_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    void *p = nullptr;  // the current device is `dev`: this resolves its own copy
+    scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_status[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = scratch_ptr[dev];
+  return scratch_status[dev];
 }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,

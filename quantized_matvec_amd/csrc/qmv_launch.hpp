@@ -29,6 +29,11 @@ hipError_t launch_quantize_4bit(const void *W, int w_dtype, int64_t numel, int l
 
 size_t double_quant_workspace_bytes(int64_t nblocks);
 
+// The allocation-free double quantization: most scales it takes, and its
+// per-device scratch (at least double_quant_workspace_bytes of that many).
+constexpr int64_t kNoAllocMaxBlocks = int64_t(1) << 24;
+hipError_t double_quant_scratch(void **ptr);
+
 // ws: double_quant_workspace_bytes(nblocks) bytes for the partial sums.
 // linear: code2 is the default table (k - 127) / 127.
 hipError_t launch_double_quant(const float *absmax, int64_t nblocks, int log2bs2,

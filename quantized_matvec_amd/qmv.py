@@ -28,7 +28,7 @@ library_path = os.path.join(_HERE, "libqmv.so")
 
 STATUS = {0: "QMV_OK", -1: "QMV_ERR_INVALID_ARG", -2: "QMV_ERR_UNSUPPORTED",
           -3: "QMV_ERR_ALIGNMENT", -4: "QMV_ERR_LAUNCH", -5: "QMV_ERR_HIP",
-          -6: "QMV_ERR_WORKSPACE"}
+          -6: "QMV_ERR_WORKSPACE", -7: "QMV_ERR_TOO_LARGE"}
 _QT = {"nf4": 0, "fp4": 1}
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         "qmv_quantize_4bit": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, ctypes.c_int, vp, vp, vp]),
         "qmv_double_quant_workspace": (sz, [i64, i32]),
         "qmv_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "qmv_double_quant_noalloc": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, vp, vp]),
         "qmv_dequantize_absmax": (ctypes.c_int, [ap, i64, vp, vp]),
         "qmv_dequantize_4bit": (ctypes.c_int, [vp, ap, i64, i32, ctypes.c_int, vp, ctypes.c_int, vp]),
         "qmv_gemv_4bit": (ctypes.c_int, [vp, ctypes.c_int, i32, i64, i64, vp, ap, i32,

@@ -34,7 +34,8 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 16 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
+    assert len(names) == 17 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
+    assert "qmv_double_quant_noalloc" in names
     for n in names:
         assert hasattr(qmvlib, n), n
 
@@ -80,6 +81,12 @@ def test_double_quant_preconditions(qmvlib):
     assert qmvlib.qmv_double_quant_workspace(0, 256) == 0
     assert qmvlib.qmv_double_quant_workspace(1000, 48) == 0
     assert qmvlib.qmv_dynamic_code2(None) == INVALID
+    g = qmvlib.qmv_double_quant_noalloc
+    assert g(P, (1 << 24) + 1, 256, None, P, P, P, P, None) == -7     # QMV_ERR_TOO_LARGE
+    assert g(P, 0, 256, None, P, P, P, P, None) == INVALID
+    assert g(P, 1000, 48, None, P, P, P, P, None) == UNSUPPORTED
+    assert g(MIS, 1000, 256, None, P, P, P, P, None) == ALIGN
+    assert qmvlib.qmv_status_string(-7)
     args = lambda **k: dict(dict(a=P, n=1000, bs2=256, code=None, q=P, a2=P, off=P, c2o=P, w=P2, wsb=ws), **k)
     call = lambda d: f(d["a"], d["n"], d["bs2"], d["code"], d["q"], d["a2"], d["off"], d["c2o"], d["w"], d["wsb"], None)
     assert call(args(n=0)) == INVALID
