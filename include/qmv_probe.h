@@ -29,6 +29,21 @@ extern "C" {
  */
 int qmv_stream_read(const void *p, int64_t bytes, uint32_t *sink, void *stream);
 
+/*
+ * gemm_4bit_plan: host-side introspection of qmv_gemm_4bit with 16-bit
+ * activations, computed by the same code that picks the kernel and maps
+ * workgroups to tiles at launch.  No device is touched.
+ *   M, N, K, blocksize  as for qmv_gemm_4bit (same argument checks)
+ *   tiles   host [4 * cap] int64 out: for workgroup w, the rectangle of C it
+ *           writes, {row0, col0, rows, cols} (it reads the same rows of A
+ *           and the same rows of the weight); NULL with cap = 0 to count
+ *   kernel  host out: 0 narrow (M <= 16), 1 split-K (M <= 64), 2 tile,
+ *           3 large-M (128 x 256 tiles, weights decoded in registers)
+ * Returns the number of workgroups (>= 0), or a negative qmv.h status.
+ */
+int64_t qmv_gemm_4bit_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int64_t *tiles,
+                           int64_t cap, int32_t *kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -345,6 +345,17 @@ int qmv_stream_read(const void *p, int64_t bytes, uint32_t *sink, void *stream) 
   return launch_status(launch_stream_read(p, bytes, sink, (hipStream_t)stream));
 }
 
+int64_t qmv_gemm_4bit_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int64_t *tiles,
+                           int64_t cap, int32_t *kernel) {
+  const int rc = check_matmul(M, N, K, blocksize, QMV_NF4);
+  if (rc != QMV_OK) return rc;
+  if (!kernel || cap < 0 || (cap > 0 && !tiles)) return QMV_ERR_INVALID_ARG;
+  int kind = 0;
+  const int64_t n = gemm_plan(M, N, K, log2_exact(blocksize), tiles, cap, &kind);
+  *kernel = kind;
+  return n;
+}
+
 int qmv_code_table(qmv_quant_type quant_type, float out16[16]) {
   if (!out16 || !valid_qt(quant_type)) return QMV_ERR_INVALID_ARG;
   const uint32_t *bits = table_bits(quant_type);

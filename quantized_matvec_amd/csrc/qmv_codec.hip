@@ -25,48 +25,7 @@ int log2_exact(int64_t v) {
   return l;
 }
 
-// ---------------------------------------------------------------------------
-// Directed conversions used to turn an exact float64 threshold into an fp32
-// one that makes a single fp32 comparison exact.
-// ---------------------------------------------------------------------------
-// Written with selects only (no branches: they run once per threshold of
-// every block, in divergent lanes).
-//
-// Bits of the largest fp32 below f (f finite; below +-0 is -denorm_min).
-__device__ __forceinline__ uint32_t f32_step_down_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t away = (u >> 31) ? u + 1u : u - 1u;  // one step toward -inf
-  return (u & 0x7fffffffu) == 0u ? 0x80000001u : away;
-}
-
-// Largest fp32 <= d.
-__device__ __forceinline__ float f64_to_f32_rd(double d) {
-  const float f = (float)d;  // round to nearest even
-  return (double)f > d ? __uint_as_float(f32_step_down_bits(f)) : f;
-}
-
-// Smallest fp32 >= d.
-__device__ __forceinline__ float f64_to_f32_ru(double d) {
-  const float f = (float)d;
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t up = (u & 0x7fffffffu) == 0u ? 1u : ((u >> 31) ? u - 1u : u + 1u);
-  return (double)f < d ? __uint_as_float(up) : f;
-}
-
-// The fp32 threshold of the exact product p = absmax * mid: RD(p) when
-// mid > 0, pred(RU(p)) when mid < 0 (both roundings computed, one selected).
-__device__ __forceinline__ float threshold_f32(double p, bool pos) {
-  const float f = (float)p;  // round to nearest even
-  const double back = (double)f;
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t down = f32_step_down_bits(f);
-  const uint32_t rd = back > p ? down : u;                          // RD(p)
-  const uint32_t up = (u & 0x7fffffffu) == 0u ? 1u : ((u >> 31) ? u - 1u : u + 1u);
-  const uint32_t ru = back < p ? up : u;                            // RU(p)
-  return __uint_as_float(pos ? rd : f32_step_down_bits(__uint_as_float(ru)));
-}
-
-// Rank among the thresholds (0..15 for NF4, 0..14 for FP4) -> code.
+// Rank among the midpoints (0..15 for NF4, 0..14 for FP4) -> code.
 template <int QT>
 __device__ __forceinline__ uint32_t rank_to_code(int r) {
   if constexpr (QT == kNF4) {
@@ -85,35 +44,35 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
 // (E = 16: a 32-byte load for 16-bit inputs); G = blocksize / E neighbouring
 // threads share a block.  The block absmax is reduced across those G threads
 // (DPP moves within rows of 16 lanes, shuffles beyond, LDS when a block spans
-// waves).  The per-block threshold sets are double-buffered, so a tile needs
-// one barrier.
+// waves).
 //
-// Exact thresholds.  For each block the fp32 thresholds are derived from the
-// exact float64 products absmax * mid[j] (mid: midpoints of adjacent distinct
-// code values):
-//   mid > 0: x moves up past the threshold only when x > absmax * mid (a tie
-//            stays with the smaller magnitude); for fp32 x that is
-//            x > RD(absmax * mid);
-//   mid < 0: x moves up when x >= absmax * mid, i.e. x > pred(RU(absmax * mid)).
-// The code is the number of thresholds x exceeds (its rank), mapped to the
-// table's code.  The G threads of a block compute its thresholds together
-// and leave them in LDS as [-inf, t_0, ..., t_last, +inf].
+// Nearest code, exactly.  Let m_0 < m_1 < ... be the midpoints of adjacent
+// distinct code values.  The code of x in a block with absmax a is its rank:
+// the number of midpoints it lies above, where "above" a positive midpoint
+// means x > a m_j (a tie stays with the smaller magnitude) and above a
+// negative one x >= a m_j.
 //
-// Rank.  n = x / absmax is approximated in fp32 and placed in a bin of
-// width 1 / S: bin = floor(S n + O).  The host picks S and O so that every
-// bin holds at most one midpoint and every midpoint lies well inside its bin
-// (at least a few hundredths of a bin from either edge, against an error in
-// S n + O of a few millionths).  With J(b) = the number of thresholds below
-// the lower edge of bin b, the rank of x is J(b) + [x > t_J(b)]: when the bin
-// holds threshold J(b) the compare decides it exactly; when it holds none,
-// t_J(b) lies above the bin and the compare is false.  An element whose
-// approximate n falls in the neighbouring bin is within a few millionths of
-// an edge, where no threshold is, so the count is the same.  t_NT = +inf.
+// The rank is read off a bin position.  t = S x / a + O is approximated in
+// fp32 as fma(x, S rcp(a), O); bin = floor(t).  The host picks S and O so
+// that every bin holds at most one midpoint, none within 0.02 of a bin edge,
+// and tabulates per bin J(b) = the midpoints below it and pos(b) = S m_J + O
+// for the midpoint inside it (+inf when there is none).  Then
+//   rank = J(b) + [t > pos(b)].
+// The fp32 t is within 1e-5 of the exact S x / a + O (rcp is within an ulp,
+// the rest one rounding each; |t| < 64) and pos(b) within 2e-6 of the exact
+// S m_J + O, so whenever |t - pos(b)| >= 2^-15 the comparison has the exact
+// answer; an element whose approximate t falls in a neighbouring bin sits
+// within 1e-5 of a bin edge, where no midpoint is, so the count is the same.
+// The few elements inside the 2^-15 band (exact ties among them) are decided
+// exactly in float64: a m_J is exact there (24 x 29 significant bits), as is
+// the comparison with x.
 // ---------------------------------------------------------------------------
 constexpr int kQBins = 64;
+constexpr float kQBand = 0x1p-15f;  // certificate band around a midpoint, in bins
 struct QuantArgs {
   Midpoints4 mids;
-  uint8_t cand[256];     // J(b); bins 64 .. 255 (clamped) count every midpoint
+  uint8_t cand[256];     // J(b); bins 64 .. 255 count every midpoint
+  float pos[256];        // pos(b), +inf for a bin without a midpoint
   float bin_scale;       // S
   float bin_offset;      // O
 };
@@ -125,25 +84,20 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
                                                             uint8_t *__restrict__ packed,
                                                             float *__restrict__ absmax) {
   using T = typename Storage<DT>::type;
-  constexpr int NT = QT == kNF4 ? 15 : 14;  // thresholds (FP4's +0 and -0 are one value)
-  constexpr int TS = 17;                    // LDS floats per block: sentinels + thresholds
   const T *W = static_cast<const T *>(Wv);
-  // two sets, used by alternate tiles: a tile's thresholds are rewritten
-  // only after every thread has passed the next tile's barrier
-  __shared__ float wave_max[2][4];
-  __shared__ float thr[2][256 * E / 32 * TS];  // up to tile / 32 blocks per tile
-  __shared__ uint8_t cand[256];  // bytes: the bin is the address
+  __shared__ float wave_max[2][4];  // blocks spanning waves, alternate tiles
+  __shared__ uint8_t cand[256];     // bytes: the bin is the address
+  __shared__ float pos[256];
   __shared__ double mids[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int G = (1 << log2bs) / E;  // threads per block: 2 .. 256
-  const int j_in_blk = tid & (G - 1);
-  const int blk_in_tile = tid / G;
   const int64_t tile = 256 * E;
   const int64_t ntiles = (numel + tile - 1) / tile;
   cand[tid] = qa.cand[tid];
-  if (tid < NT) mids[tid] = qa.mids.mid[tid];
+  pos[tid] = qa.pos[tid];
+  if (tid < 15) mids[tid] = qa.mids.mid[tid];
   __syncthreads();
 
   // full tiles' loads: E elements per thread as raw 16-byte words (E / 4
@@ -191,53 +145,52 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       for (int i = 1; i < wpb; ++i) mm = fmaxf(mm, wave_max[par][w0 + i]);
       m = mm;
     }
-    if (FULL || (j_in_blk == 0 && e0 < numel)) absmax[e0 >> log2bs] = m;
+    if (FULL || ((tid & (G - 1)) == 0 && e0 < numel)) absmax[e0 >> log2bs] = m;
 
-    // this block's thresholds, shared out among its G threads
-    float *bt = thr[par] + blk_in_tile * TS;
-    const double ad = (double)m;
-    for (int j = j_in_blk; j < NT; j += G) {
-      const double mid = mids[j];
-      const double p = ad * mid;  // exact
-      bt[1 + j] = threshold_f32(p, mid > 0.0);
-    }
-    if (j_in_blk == 0) {
-      bt[0] = -INFINITY;
-      bt[NT + 1] = INFINITY;
-    }
-    __syncthreads();
-
-    // approximate n = x / absmax: tiny blocks are scaled up by 2^100 (exact)
-    // so the reciprocal stays finite, huge ones down by 2^100 so it stays
-    // normal (only the candidate uses n); an all-zero block has n = 0
+    // t = S x / a + O: tiny blocks are scaled up by 2^100 (exact) so the
+    // reciprocal stays finite, huge ones down by 2^100 so it stays normal;
+    // an all-zero block has t = O, the position of 0
     const float sc = m < 0x1p-100f ? 0x1p100f : (m > 0x1p100f ? 0x1p-100f : 1.f);
     const float inv = m > 0.f ? qa.bin_scale * __builtin_amdgcn_rcpf(m * sc) : 0.f;
-    // in phases, so that the 16 table reads of a phase are in flight together.
-    // bin = floor(S n + O), except within 1/256 below an integer where it is
-    // that integer (harmless: no midpoint lies within 0.02 of a bin edge),
-    // clamped to 0 .. 255 by the conversion: v_cvt_pk_u8_f32 rounds
-    // S n + O - 1/2 + 1/256 to the nearest integer and saturates
-    const float off = qa.bin_offset - 0.5f + 0x1p-8f;  // exact
-    int cb[E];
+    const float O = qa.bin_offset;
+    float tq[E];
     if (__builtin_amdgcn_ballot_w64(sc != 1.f) == 0) {  // wave-uniform: no rescaled block
 #pragma unroll
-      for (int i = 0; i < E; ++i) cb[i] = (int)__builtin_amdgcn_cvt_pk_u8_f32(fmaf(v[i], inv, off), 0, 0u);
+      for (int i = 0; i < E; ++i) tq[i] = fmaf(v[i], inv, O);
     } else {
 #pragma unroll
-      for (int i = 0; i < E; ++i)
-        cb[i] = (int)__builtin_amdgcn_cvt_pk_u8_f32(fmaf(v[i] * sc, inv, off), 0, 0u);
+      for (int i = 0; i < E; ++i) tq[i] = fmaf(v[i] * sc, inv, O);
     }
-#pragma unroll
-    for (int i = 0; i < E; ++i) cb[i] = (int)cand[cb[i]];
-    float tb[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) tb[i] = bt[1 + cb[i]];
-    uint32_t code[E];
+    int J[E];
+    float pb[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const int r = cb[i] + (v[i] > tb[i] ? 1 : 0);
-      code[i] = (FULL || e0 + i < numel) ? rank_to_code<QT>(r) : 0u;
+      const uint32_t b = (uint32_t)tq[i];  // floor: t >= 1 (clamped into the table)
+      J[i] = (int)cand[b & 255u];
+      pb[i] = pos[b & 255u];
     }
+    uint32_t rank[E];
+    uint32_t amb = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      rank[i] = (uint32_t)J[i] + (tq[i] > pb[i] ? 1u : 0u);
+      amb |= (fabsf(tq[i] - pb[i]) < kQBand ? 1u : 0u) << i;
+    }
+    if (__builtin_amdgcn_ballot_w64(amb != 0) != 0) {  // rare: decide the band exactly
+      const double ad = (double)m;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if ((amb >> i) & 1u) {
+          const double mid = mids[J[i]];
+          const double p = ad * mid;  // exact
+          const double xd = (double)v[i];
+          rank[i] = (uint32_t)J[i] + ((mid > 0.0 ? xd > p : xd >= p) ? 1u : 0u);
+        }
+      }
+    }
+    uint32_t code[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) code[i] = (FULL || e0 + i < numel) ? rank_to_code<QT>((int)rank[i]) : 0u;
 
     uint32_t word[E / 8];
 #pragma unroll
@@ -340,6 +293,9 @@ static bool bin_geometry(const Midpoints4 &m, int nt, QuantArgs &qa) {
     for (int j = 0; j < nt; ++j)
       c += std::floor((double)qa.bin_scale * m.mid[j] + (double)qa.bin_offset) < b ? 1 : 0;
     qa.cand[b] = (uint8_t)c;
+    // the midpoint inside bin b, if any, is midpoint c
+    const double pj = c < nt ? (double)qa.bin_scale * m.mid[c] + (double)qa.bin_offset : 0.0;
+    qa.pos[b] = (c < nt && std::floor(pj) == (double)b) ? (float)pj : INFINITY;
   }
   return true;
 }

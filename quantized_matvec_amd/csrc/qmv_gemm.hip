@@ -774,6 +774,295 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_f32_kernel(const float *__re
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large M (M >= 448): gemm_4bit_rb_kernel
+//
+// A workgroup of 4 waves owns a 128 (M) x 256 (N) tile of C; wave w computes
+// all 128 rows x columns [64 w, 64 w + 64) as 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16 (f16), one wave per SIMD.  Per k-tile of 64:
+//  * the activations go global -> LDS with 16-byte LDS-direct loads into a
+//    3-stage ring (128 rows x 128 B per stage; a row's 16-byte chunks are
+//    XOR-swizzled by row % 8, so the MFMA operand reads of 32 rows spread
+//    over all banks), issued two k-tiles ahead;
+//  * each wave decodes its own weights straight into MFMA operand registers
+//    (no LDS tile for the weights): lane l covers column 32 j + l % 32 and the
+//    32 k-values 32 (l / 32) .. + 31 (one 16-byte packed load), so MFMA t
+//    takes its k-values 8 t .. 8 t + 7 (the activations are read in the same
+//    order).  A packed byte is one v_perm_b32 (its LDS address) and one
+//    ds_read_b64 of a 64 KB table of fp32 pairs (T[hi], T[lo]) with 32
+//    copies, one per lane of a half-wave (no bank conflicts); the weights
+//    are fp32(T * a_hat) rounded to the input type, exactly the
+//    dequantize_4bit values;
+//  * the next k-tile's packed weights and scales are loaded meanwhile.
+// Workgroups are ordered so that the row tiles of one column tile run on one
+// XCD (dispatch is round-robin over the 8 XCDs): its packed weights are read
+// from HBM once and then from that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kRbM = 128, kRbN = 256, kRbK = 64;
+
+// Tile (row, column origin) of workgroup `id` of the large-M kernel.
+__host__ __device__ inline void rb_tile(int id, int ncol, int nrow, int64_t &m0, int64_t &n0) {
+  int cb, rb;
+  if (ncol % 8 == 0) {  // XCD k = id % 8 takes column tiles k, k + 8, ..., each for every row tile
+    const int xcd = id & 7, s = id >> 3;
+    cb = xcd + 8 * (s / nrow);
+    rb = s % nrow;
+  } else {
+    cb = id % ncol;
+    rb = id / ncol;
+  }
+  m0 = (int64_t)rb * kRbM;
+  n0 = (int64_t)cb * kRbN;
+}
+
+// A buffer resource with its base and size made wave-uniform explicitly (they
+// are uniform already; this keeps the descriptor in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return make_rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
+
+template <int ADT, int CDT, bool DQ>
+__global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
+    const uint16_t *__restrict__ A, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    Scales sc, int log2bs, Table16f table, void *__restrict__ Cv, const void *__restrict__ biasv,
+    int ncol, int nrow) {
+  using CT = typename Storage<CDT>::type;
+  CT *C = static_cast<CT *>(Cv);
+  const CT *bias = static_cast<const CT *>(biasv);
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 32 * 2];  // byte -> (T[hi], T[lo]), 32 copies
+  __shared__ float code2[256];
+  // one array per ring stage, so that the compiler can tell an LDS-direct
+  // load into one stage from reads of another
+  __shared__ uint4 st0[kRbM * 8], st1[kRbM * 8], st2[kRbM * 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t m0, n0;
+  rb_tile((int)blockIdx.x, ncol, nrow, m0, n0);
+  const int KT = (int)(K / kRbK);
+  {  // table: 16-byte chunk c holds copies 2 (c % 16) and + 1 of entry c / 16
+    const uint32_t lo = __float_as_uint(table.v[(tid >> 4) & 15]);
+    uint4 *dst = reinterpret_cast<uint4 *>(lut);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const uint32_t hi = __float_as_uint(table.v[it]);
+      dst[it * 256 + tid] = make_uint4(hi, lo, hi, lo);
+    }
+  }
+  float offset = 0.f;
+  if constexpr (DQ) {
+    code2[tid] = sc.code2[tid];
+    offset = sc.offset[0];
+  }
+  // activations: wave w moves rows (4 w + d) * 8 + l / 8 of a stage, lane l
+  // into position l % 8 of its row, from chunk (l % 8) ^ (row % 8); rows
+  // past M read zeros (bounded resource)
+  const int64_t mrows = M - m0 < kRbM ? M - m0 : kRbM;
+  const uint16_t *a_base = A + m0 * K;
+  const uint32_t a_bytes = (uint32_t)(mrows * K * 2);
+  uint32_t aoff[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int r = (4 * wave + d) * 8 + (lane >> 3);
+    aoff[d] = (uint32_t)(r * K * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+  }
+  auto issue_a = [&](int kt, uint4 *stage) {  // k-tiles past the end re-read the last one
+    const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * (kRbK * 2);
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc_u(a_base, a_bytes);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) load_lds16(ars, stage + (4 * wave + d) * 64, aoff[d] + ko);
+  };
+  // weights: lane -> columns n0 + 64 w + 32 j + l % 32 (j = 0, 1), k half h = l / 32;
+  // columns past N read zeros, and their scales are the last column's
+  const int h = lane >> 5, colw = lane & 31;
+  const int64_t ncols = N - n0 < kRbN ? N - n0 : kRbN;
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const uint8_t *p_base = packed + n0 * (int64_t)rowb;
+  const uint32_t p_bytes = (uint32_t)(ncols * rowb);
+  const int64_t bpr = K >> log2bs;  // blocks per weight row
+  uint32_t boff[2];
+  int64_t scol[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 64 * wave + 32 * j + colw;
+    boff[j] = (uint32_t)c * rowb + 16u * h;
+    scol[j] = n0 + c < N ? n0 + c : N - 1;
+  }
+  struct BR {
+    uint4 w[2];
+    uint32_t q[2];
+    float s[2];
+  };
+  auto issue_b = [&](int kt, BR &b) {
+    const int kc = kt < KT ? kt : KT - 1;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc_u(p_base, p_bytes);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      b.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, boff[j] + (uint32_t)kc * 32u, 0, 0));
+      const int64_t blk = scol[j] * bpr + (((int64_t)kc * kRbK + 32 * h) >> log2bs);
+      if constexpr (DQ) {
+        b.q[j] = sc.q[blk];
+        b.s[j] = sc.absmax2[blk >> sc.log2bs2];
+      } else {
+        b.s[j] = sc.absmax[blk];
+      }
+    }
+  };
+  issue_a(0, st0);
+  issue_a(1, st1);
+  BR br0, br1;
+  issue_b(0, br0);
+  __syncthreads();  // table and code2
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const uint32_t lane_sel = (uint32_t)colw << 3;
+  const char *lut_b = reinterpret_cast<const char *>(lut);
+  auto decode = [&](const BR &b, bf16x8_t (&bf)[2][4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // the 16 table reads of the column first, then the arithmetic
+      float2 tv[16];
+#pragma unroll
+      for (int bb = 0; bb < 16; ++bb) {
+        const uint32_t w = bb < 4 ? b.w[j].x : bb < 8 ? b.w[j].y : bb < 12 ? b.w[j].z : b.w[j].w;
+        const uint32_t addr = __builtin_amdgcn_perm(w, lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
+        tv[bb] = *reinterpret_cast<const float2 *>(lut_b + addr);
+      }
+      const float a = DQ ? code2[b.q[j] & 255u] * b.s[j] + offset : b.s[j];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // MFMA t: bytes 4 t .. 4 t + 3 (k 32 h + 8 t .. + 7)
+        uint32_t o[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) o[bb] = cvt_pair<ADT>(tv[4 * t + bb].x * a, tv[4 * t + bb].y * a);
+        bf[j][t] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    }
+  };
+  auto mma = [&](const uint4 *stage, const bf16x8_t (&bf)[2][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 4 * h + t;  // this lane's 16-byte chunk of the row for MFMA t
+      bf16x8_t af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + colw;
+        af[i] = __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ (r & 7))]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<ADT>(af[i], bf[j][t], acc[i][j]);
+    }
+  };
+  // iteration kt: A(kt) in stage kt % 3, B(kt) in register set kt % 2
+  auto step = [&](int kt, uint4 *sa_cur, uint4 *sa_next2, BR &bcur, BR &bnext) {
+    // A(kt) must have landed for every wave: this wave's loads issued since
+    // are A(kt + 1) (4) and B(kt) (2 + 4, or 2 + 2 without double quantization)
+    constexpr int after = 4 + (DQ ? 6 : 4);
+    __builtin_amdgcn_s_waitcnt((after & 15) | (7 << 4) | (15 << 8) | ((after >> 4) << 14));
+    __syncthreads();  // and every wave is done with stage (kt + 2) % 3
+    issue_a(kt + 2, sa_next2);
+    issue_b(kt + 1, bnext);
+    bf16x8_t bf[2][4];
+    decode(bcur, bf);
+    mma(sa_cur, bf);
+  };
+  int kt = 0;
+  for (; kt + 6 <= KT; kt += 6) {
+    step(kt, st0, st2, br0, br1);
+    step(kt + 1, st1, st0, br1, br0);
+    step(kt + 2, st2, st1, br0, br1);
+    step(kt + 3, st0, st2, br1, br0);
+    step(kt + 4, st1, st0, br0, br1);
+    step(kt + 5, st2, st1, br1, br0);
+  }
+  {  // the remaining 0..5 k-tiles (kt is a multiple of 6 here)
+    const int rem = KT - kt;
+    if (rem > 0) step(kt, st0, st2, br0, br1);
+    if (rem > 1) step(kt + 1, st1, st0, br1, br0);
+    if (rem > 2) step(kt + 2, st2, st1, br0, br1);
+    if (rem > 3) step(kt + 3, st0, st2, br1, br0);
+    if (rem > 4) step(kt + 4, st1, st0, br0, br1);
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no LDS-direct load outlives the kernel
+
+  // 32 x 32 accumulator layout: column = lane % 32, row = 8 (r / 4) + 4 (lane / 32) + r % 4
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + 64 * wave + 32 * j + colw;
+      if (col >= N) continue;
+      const float bv = bias ? load_elem<CDT>(bias, col) : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < M) store_elem<CDT>(C, row * N + col, bias ? acc[i][j][r] + bv : acc[i][j][r]);
+      }
+    }
+}
+
+// Which kernel gemm_4bit runs for 16-bit activations, and its grid.
+// kind 0: narrow, 1: skinny (both: N / 32 workgroups, each all M rows of 32
+// columns); 2: tile kernel (grid x over N tiles of bn, y over M tiles of bm);
+// 3: large-M kernel (gx workgroups mapped by rb_tile).
+struct GemmChoice {
+  int kind;
+  int bm, bn;
+  int64_t gx, gy;
+};
+
+GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, int log2bs) {
+  if (gemm_narrow_eligible(M, K, log2bs)) return {0, (int)M, 32, (N + 31) / 32, 1};
+  if (M <= 64 && K % 64 == 0 && K < (1 << 23)) return {1, (int)M, 32, (N + 31) / 32, 1};
+  if (gemm_rb_eligible(M, N, K)) {
+    const int64_t ncol = (N + kRbN - 1) / kRbN, nrow = (M + kRbM - 1) / kRbM;
+    return {3, kRbM, kRbN, ncol * nrow, 1};
+  }
+  // 256 x 128 tiles when they still give a workgroup to most compute units,
+  // else 128 x 128, else 128 x 64 (narrower tiles, more workgroups)
+  const int64_t cus = device_cu_count();
+  const int64_t nt128 = (N + 127) / 128;
+  const int shape = nt128 * ((M + 255) / 256) >= cus * 3 / 4 ? 2 : (nt128 * ((M + 127) / 128) >= cus ? 1 : 0);
+  const int bm = shape == 2 ? 256 : 128, bn = shape ? 128 : 64;
+  return {2, bm, bn, (N + bn - 1) / bn, (M + bm - 1) / bm};
+}
+
+// Host-side: the C tile [row0, row0 + rows) x [col0, col0 + cols) each
+// workgroup of gemm_4bit's launch writes (it reads the same rows of A),
+// computed with the kernels' own tile mapping.  Returns the number of
+// workgroups; tiles gets 4 values per workgroup, up to cap of them.
+int64_t gemm_plan(int64_t M, int64_t N, int64_t K, int log2bs, int64_t *tiles, int64_t cap, int *kind) {
+  const GemmChoice g = gemm_choice(M, N, K, log2bs);
+  *kind = g.kind;
+  const int64_t nwg = g.gx * g.gy;
+  for (int64_t w = 0; w < nwg && w < cap; ++w) {
+    int64_t m0, n0;
+    if (g.kind == 3) {
+      rb_tile((int)w, (int)((N + kRbN - 1) / kRbN), (int)((M + kRbM - 1) / kRbM), m0, n0);
+    } else {
+      m0 = (w / g.gx) * g.bm;
+      n0 = (w % g.gx) * g.bn;
+    }
+    int64_t *t = tiles + 4 * w;
+    t[0] = m0;
+    t[1] = n0;
+    t[2] = M - m0 < g.bm ? M - m0 : g.bm;
+    t[3] = N - n0 < g.bn ? N - n0 : g.bn;
+  }
+  return nwg;
+}
+
 template <int ADT>
 static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
                                 const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
@@ -782,8 +1071,9 @@ static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
   Table16f table;
   const uint32_t *bits = table_bits(qt);
   for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
-  if (gemm_narrow_eligible(M, K, log2bs)) {  // narrow M
-    const dim3 sgrid((unsigned)((N + 31) / 32));
+  const GemmChoice g = gemm_choice(M, N, K, log2bs);
+  if (g.kind == 0) {  // narrow M
+    const dim3 sgrid((unsigned)g.gx);
 #define QMV_N(CDT, DQV, MPV, NBV, KWV)                                                          \
   hipLaunchKernelGGL((gemm_4bit_narrow_kernel<ADT, CDT, DQV, MPV, NBV, KWV>), sgrid, dim3(64 * KWV), \
                      0, st, a, M, N, K, packed, sc, log2bs, table, C, bias)
@@ -800,8 +1090,8 @@ static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
 #undef QMV_N
     return hipGetLastError();
   }
-  if (M <= 64 && K % 64 == 0 && K < (1 << 23)) {  // skinny M: N / 32 workgroups of 8 waves splitting K
-    const dim3 sgrid((unsigned)((N + 31) / 32));
+  if (g.kind == 1) {  // skinny M: N / 32 workgroups of 8 waves splitting K
+    const dim3 sgrid((unsigned)g.gx);
 #define QMV_S(CDT, DQV, MTV)                                                                   \
   hipLaunchKernelGGL((gemm_4bit_skinny_kernel<ADT, CDT, DQV, MTV, 8>), sgrid, dim3(512), 0, st, a, \
                      M, N, K, packed, sc, log2bs, table, C, bias)
@@ -817,13 +1107,23 @@ static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
 #undef QMV_S
     return hipGetLastError();
   }
-  // 256 x 128 tiles when they still give a workgroup to most compute units,
-  // else 128 x 128, else 128 x 64 (narrower tiles, more workgroups)
-  const int64_t cus = device_cu_count();
-  const int64_t nt128 = (N + 127) / 128;
-  const int shape = nt128 * ((M + 255) / 256) >= cus * 3 / 4 ? 2 : (nt128 * ((M + 127) / 128) >= cus ? 1 : 0);
-  const dim3 grid((unsigned)(shape ? nt128 : (N + 63) / 64),
-                  (unsigned)(shape == 2 ? (M + 255) / 256 : (M + 127) / 128));
+  if (g.kind == 3) {  // large M: 128 x 256 tiles, weights decoded in registers
+    const int ncol = (int)((N + kRbN - 1) / kRbN), nrow = (int)((M + kRbM - 1) / kRbM);
+    const dim3 rgrid((unsigned)g.gx);
+#define QMV_R(CDT, DQV)                                                                            \
+  hipLaunchKernelGGL((gemm_4bit_rb_kernel<ADT, CDT, DQV>), rgrid, dim3(256), 0, st, a, M, N, K, packed, \
+                     sc, log2bs, table, C, bias, ncol, nrow)
+#define QMV_RD(CDT) \
+  if (dq) { QMV_R(CDT, true); } else { QMV_R(CDT, false); }
+    if (c_dtype == kF32) { QMV_RD(kF32); }
+    else if (c_dtype == kF16) { QMV_RD(kF16); }
+    else { QMV_RD(kBF16); }
+#undef QMV_RD
+#undef QMV_R
+    return hipGetLastError();
+  }
+  const int shape = g.bm == 256 ? 2 : (g.bn == 128 ? 1 : 0);
+  const dim3 grid((unsigned)g.gx, (unsigned)g.gy);
 #define QMV_M(CDT, DQV, BMV, BNV)                                                                    \
   hipLaunchKernelGGL((gemm_4bit_kernel<ADT, CDT, DQV, BMV, BNV>), grid, dim3(2 * BMV), 0, st, a, M, N, \
                      K, packed, sc, log2bs, table, C, bias)

@@ -65,6 +65,15 @@ int resident_wgs_per_cu(const void *kernel, int threads);
 inline bool gemm_narrow_eligible(int64_t M, int64_t K, int log2bs) {
   return M <= 16 && log2bs >= 6 && K % 64 == 0 && K < (1 << 23);
 }
+// True when gemm_4bit takes its large-M kernel (128 x 256 tiles): at least
+// 448 rows (four row tiles: the grid covers most compute units), K a
+// multiple of 64 and its offsets within 32 bits.
+inline bool gemm_rb_eligible(int64_t M, int64_t N, int64_t K) {
+  return M >= 448 && K % 64 == 0 && K < (1 << 22) &&
+         ((N + 255) / 256) * ((M + 127) / 128) < ((int64_t)1 << 31);
+}
+// Host-side launch plan of gemm_4bit (16-bit activations): see qmv_gemm.hip.
+int64_t gemm_plan(int64_t M, int64_t N, int64_t K, int log2bs, int64_t *tiles, int64_t cap, int *kind);
 // a_dtype: kBF16 or kF16 (the matrix cores' input type); bias as for gemv.
 hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, int64_t K,
                             const uint8_t *packed, const Scales &sc, bool dq, int log2bs, int qt,

@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         "qmv_embedding_4bit": (ctypes.c_int, [vp, i64, i64, i64, vp, ap, i32, ctypes.c_int, vp,
                                               ctypes.c_int, vp]),
         "qmv_stream_read": (ctypes.c_int, [vp, i64, vp, vp]),
+        "qmv_gemm_4bit_plan": (i64, [i64, i64, i64, i32, vp, i64, vp]),
         "qmv_code_table": (ctypes.c_int, [ctypes.c_int, vp]),
         "qmv_default_code2": (ctypes.c_int, [vp]),
         "qmv_dynamic_code2": (ctypes.c_int, [vp]),

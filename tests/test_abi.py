@@ -34,7 +34,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 17 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
+    assert len(names) == 18 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
     assert "qmv_double_quant_noalloc" in names
     for n in names:
         assert hasattr(qmvlib, n), n
@@ -252,3 +252,36 @@ def test_binding_refuses_mismatched_state(dq):
     packed, st = _state(dq=dq)
     with pytest.raises(ValueError, match="GPU tensor"):
         qmv.gemv_4bit(x, packed, st)
+
+
+# ---------------------------------------------------------------- gemm launch extents
+@pytest.mark.parametrize("M", [65, 200, 447, 448, 512, 1000, 1024, 2048, 4096, 4096 + 77])
+@pytest.mark.parametrize("N", [14336, 1000, 28672])
+def test_gemm_tiles_cover_the_output_once_within_bounds(qmvlib, M, N):
+    """The workgroup tiles of gemm_4bit's launch (from the launcher's own
+    choice and tile mapping): every one lies inside [0, M) x [0, N), so no
+    workgroup reads a row of A past M * K or writes C past M * N, and
+    together they cover every output exactly once."""
+    K = 4096
+    kind = ctypes.c_int32(-1)
+    n = qmvlib.qmv_gemm_4bit_plan(M, N, K, 64, None, 0, ctypes.byref(kind))
+    assert n > 0
+    tiles = (ctypes.c_int64 * (4 * n))()
+    assert qmvlib.qmv_gemm_4bit_plan(M, N, K, 64, tiles, n, ctypes.byref(kind)) == n
+    assert kind.value == (3 if M >= 448 else 2)
+    t = np.array(tiles, dtype=np.int64).reshape(n, 4)
+    r0, c0, nr, nc = t.T
+    assert (r0 >= 0).all() and (c0 >= 0).all() and (nr > 0).all() and (nc > 0).all()
+    assert (r0 + nr <= M).all() and (c0 + nc <= N).all()          # A rows < M, C elements < M * N
+    assert int((nr * nc).sum()) == M * N                           # no overlap, given full cover below
+    cover = np.zeros((M, N), dtype=np.uint8)
+    for a, b, c, d in t:
+        cover[a:a + c, b:b + d] += 1
+    assert cover.min() == 1 and cover.max() == 1
+
+
+def test_gemm_plan_refuses_bad_shapes(qmvlib):
+    kind = ctypes.c_int32(-1)
+    assert qmvlib.qmv_gemm_4bit_plan(0, 10, 64, 64, None, 0, ctypes.byref(kind)) == INVALID
+    assert qmvlib.qmv_gemm_4bit_plan(10, 10, 96, 64, None, 0, ctypes.byref(kind)) == UNSUPPORTED
+    assert qmvlib.qmv_gemm_4bit_plan(10, 10, 64, 64, None, 0, None) == INVALID

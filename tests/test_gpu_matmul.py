@@ -241,3 +241,55 @@ def test_gemm_m1_matches_gemv():
     # both within the bf16-activation bound of the same reference, so within
     # twice it of each other
     assert rel_l2(f64(y2), f64(y1)) <= 2 * (2.0 ** -8 + (K + 16) * 2.0 ** -24)
+
+
+# ---------------------------------------------------------------- large M (128 x 256 tiles)
+@pytest.mark.parametrize("M,N,K,bs", [(448, 2048, 192, 64), (500, 1000, 4160, 64), (777, 2080, 64, 32), (640, 3000, 1024, 128),
+                                      (1030, 513, 1024, 64)])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemm_large_m_ragged(M, N, K, bs, dq):
+    """M >= 448 takes the large-M kernel: a row tile past M (500, 777, 1030),
+    column tiles past N (1000, 2080, 513; 2048 = 8 tiles of 256 takes the
+    XCD-ordered mapping), a single k-tile (K = 64), 3 k-tiles, and K = 4160 =
+    65 k-tiles (the loop's remainder path); blocks of 32, 64 and 128."""
+    W = gaussian((N, K), 0.02, M + N + dq, "bf16")
+    A = gaussian((M, K), 1.0, M + K, "bf16")
+    p_ref, ahat = oracle_state(f64(W), bs, "nf4", dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "nf4", double_quant=dq)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    Wh = w_hat(p_ref, ahat, N, K, bs, "nf4")
+    for od in (torch.bfloat16, torch.float32):
+        C = qmv.gemm_4bit(A.cuda(), packed, st, out_dtype=od)
+        assert C.shape == (M, N)
+        check_matmul(f64(C), f64(A), Wh, "bf16", od, f"M={M} N={N} K={K} dq={dq} {od}")
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+@pytest.mark.parametrize("xd", ["bf16", "fp16"])
+def test_gemm_large_m_identity_rows_exact(qt, xd):
+    """Rows of the identity among 600 rows of A: the large-M kernel multiplies
+    fp32(T * a_hat) rounded to the activations' type, so those rows return the
+    dequantize_4bit weights of that type bit for bit (a -0 weight reads +0);
+    with a bias, one fp32 addition and one rounding."""
+    M, N, K, bs = 600, 1000, 320, 64
+    W = gaussian((N, K), 0.02, 61, "bf16")
+    p_ref, a_ref = O.quantize_4bit(f64(W), bs, qt)
+    packed, st = upload_state(p_ref, a_ref, (N, K), torch.bfloat16, bs, qt)
+    A = gaussian((M, K), 1.0, 62, xd)
+    rows = np.arange(100, 100 + K)            # rows 100 .. 419 are e_0 .. e_{K-1}
+    A[torch.from_numpy(rows)] = 0
+    A[torch.from_numpy(rows), torch.arange(K)] = 1
+    C = qmv.gemm_4bit(A.cuda(), packed, st)
+    got = C.cpu().view(torch.int16).numpy().view(np.uint16)[rows]
+    want = np.asarray(O.dequantize_4bit(p_ref, a_ref, N * K, bs, qt, xd)).view(np.uint16).reshape(N, K).T.copy()
+    zero = 0x8000
+    want[want == zero] = 0
+    got = got.copy()
+    got[got == zero] = 0
+    assert np.array_equal(got, want)
+    bias = gaussian((N,), 0.5, 63, xd).cuda()
+    Cf = qmv.gemm_4bit(A.cuda(), packed, st, out_dtype=torch.float32)
+    Cb = qmv.gemm_4bit(A.cuda(), packed, st, bias=bias)
+    assert torch.equal(Cb.cpu(), (Cf + bias.float()).to(Cb.dtype).cpu())
+    Wh = w_hat(p_ref, a_ref, N, K, bs, qt)
+    check_matmul(f64(Cf), f64(A), Wh, xd, "fp32", f"{qt} {xd} fp32 out")
