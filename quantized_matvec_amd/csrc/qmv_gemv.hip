@@ -198,12 +198,16 @@ __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSim
 
   Buf b0, b1;
   if (ngroups > 0) load(0, 0, b0);
-  float offset = 0.f;
+  float offset = 0.f, c2v = 0.f;
   if constexpr (DQ) {
-    if (tid < 256) code2[tid] = sc.code2[tid];
+    c2v = sc.code2[tid & 255];
     offset = sc.offset[0];
   }
+  // the table first: it waits on no load
   build_pair_table<kGemvThreads>(lut, table, tid);
+  if constexpr (DQ) {
+    if (tid < 256) code2[tid] = c2v;
+  }
   __syncthreads();
   const uint32_t lane_sel = (uint32_t)lane << 2;
   const char *lut_bytes = reinterpret_cast<const char *>(lut);
@@ -400,6 +404,9 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
           0);
   }
 
+  // the table first: it waits on no load, so it is built while the
+  // activations and the DQ table are still on their way
+  build_pair_table<kM1Threads>(lut, table, tid);
   if constexpr (XLDS) {
     // x as 16-byte chunks, transposed: chunk q (8 values) of piece pc goes to
     // ((pc / 64) * 4 + q) * 64 + pc % 64
@@ -416,7 +423,6 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
   if constexpr (DQ) {
     if (tid < 256) code2[tid] = c2v;
   }
-  build_pair_table<kM1Threads>(lut, table, tid);
   __syncthreads();
   const uint32_t lane_sel = (uint32_t)lane << 2;
   const char *lut_bytes = reinterpret_cast<const char *>(lut);
