@@ -17,7 +17,16 @@ bf16 weight (blocksize 4096; linear and dynamic-tree tables) and an
 embedding gather (8192 random rows of a 128256 x 4096 NF4 table to bf16),
 which are not part of the step.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+The "configs" table then times every workload of the parity suite the same
+way: the fp32 1024x1024 and bf16 4096x4096 NF4 weights; W_up 14336x4096 and
+W_down 4096x14336 (NF4 and FP4, double-quantized scales); gemm_4bit at M =
+8 ... 2048 on the 14336x4096 prefill weight with gemv_4bit at M = 1 and 8 for
+the crossover; the 8192x28672 and 28672x8192 layers (NF4 and FP4, block 128,
+double-quantized scales) with gemv_4bit at M = 1, 2, 4, 8.  Each row gives
+microseconds per launch, algorithmic bytes (and flops for gemm), the fraction
+of the HBM peak and of the measured read (gemv) or copy (codec) ceiling.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-configs]
 """
 from __future__ import annotations
 
@@ -107,39 +116,222 @@ def timed_loop(fn, iters, stream, torch):
     return start.elapsed_time(end) / iters * 1e3   # microseconds per call
 
 
-def cpu_baseline(W_cpu, x_cpu, budget_s=15.0, rows=256):
-    """The oracle's gemv on a bounded sample: the first `rows` output rows of
-    the weight, single-threaded.  Untimed set-up: block scales of the whole
-    weight (the double-quant mean needs all of them), double quant, and the
-    oracle quantize of the sampled rows.  Timed, repeated until `budget_s`:
-    scale reconstruction of the sampled blocks, dequantization and the float64
-    matmul.  Bytes are counted per output row exactly as for the GPU kernel."""
+def cpu_baseline(W_cpu, x_cpu, A_cpu, budget_s=12.0, rows=256):
+    """The oracle as it stands, timed on bounded samples of the headline
+    workload (W_up 14336 x 4096 bf16, NF4, block 64, double-quantized scales):
+      quantize_4bit of the first 64 weight rows; double_quant of the first
+      65536 block scales; dequantize_4bit (to bf16) of the first `rows` rows;
+      gemv (scale decode + dequantize + float64 matmul) over the first `rows`
+      output rows, repeated for `budget_s`; gemm of 64 activation rows against
+      the first `rows` output rows.
+    Elementwise numpy runs on one thread, the float64 matmuls on all BLAS
+    threads.  Bytes and flops are counted per unit exactly as for the GPU
+    kernels.  The headline value is the gemv's."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
     W64 = W_cpu.to(torch.float64).numpy()
     x64 = x_cpu.to(torch.float64).numpy()
+    A64 = A_cpu[:64].to(torch.float64).numpy()
+    blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    ops = {}
     with threadpool_limits(limits=1):
-        absmax = O.block_absmax(W64, BS).astype(np.float32)
+        absmax = O.block_absmax(W64, BS).astype(np.float32)      # untimed set-up
         q, a2, off = O.double_quant(absmax, BS2)
+        t0 = time.perf_counter()
+        O.quantize_4bit(W64[:64], BS, "nf4")
+        t = time.perf_counter() - t0
+        ops["quantize_4bit"] = {"gbs": round(64 * K * (2 + 0.5 + 4 / BS) / t / 1e9, 5), "s": round(t, 3),
+                                "sample": "64 rows x 4096"}
+        t0 = time.perf_counter()
+        O.double_quant(absmax[:65536], BS2)
+        t = time.perf_counter() - t0
+        ops["double_quant"] = {"gbs": round(65536 * (4 + 1 + 4 / BS2) / t / 1e9, 5), "s": round(t, 3),
+                               "sample": "65536 scales"}
         packed, _ = O.quantize_4bit(W64[:rows], BS, "nf4")
         nbs = rows * K // BS
+        ahat = O.dequant_absmax(q[:nbs], a2[:-(-nbs // BS2)], off, None, BS2)
+        t0 = time.perf_counter()
+        O.dequantize_4bit(packed, ahat, rows * K, BS, "nf4", "bf16")
+        t = time.perf_counter() - t0
+        ops["dequantize_4bit"] = {"gbs": round(rows * K * (0.5 + 2 + (1 + 4 / BS2) / BS) / t / 1e9, 5),
+                                  "s": round(t, 3), "sample": f"{rows} rows x 4096"}
+    with threadpool_limits(limits=1, user_api="openmp"), threadpool_limits(limits=blas, user_api="blas"):
         passes, t0 = 0, time.perf_counter()
         while True:
-            ahat = O.dequant_absmax(q[:nbs], a2[:-(-nbs // BS2)], off, None, BS2)
-            O.matmul_4bit(x64, packed, ahat, rows, K, BS, "nf4")
+            ah = O.dequant_absmax(q[:nbs], a2[:-(-nbs // BS2)], off, None, BS2)
+            O.matmul_4bit(x64, packed, ah, rows, K, BS, "nf4")
             passes += 1
-            t = time.perf_counter() - t0
-            if t >= budget_s:
+            t_gemv = time.perf_counter() - t0
+            if t_gemv >= budget_s:
                 break
-    per_row = K // 2 + K // BS * (1 + 4 / BS2) + 2 * M_GEMV      # packed + DQ scales + y
-    gbs = passes * rows * per_row / t / 1e9
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        per_row = K // 2 + K // BS * (1 + 4 / BS2) + 2 * M_GEMV      # packed + DQ scales + y
+        gbs = passes * rows * per_row / t_gemv / 1e9
+        ops["gemv_4bit"] = {"gbs": round(gbs, 5), "s": round(t_gemv, 3),
+                            "sample": f"{rows} output rows, {passes} passes"}
+        t0 = time.perf_counter()
+        O.matmul_4bit(A64, packed, ahat, rows, K, BS, "nf4")
+        t = time.perf_counter() - t0
+        ops["gemm_4bit"] = {"gflops": round(2 * 64 * rows * K / t / 1e9, 4), "s": round(t, 3),
+                            "sample": f"64 x {rows} outputs, K = 4096"}
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": blas, "kind": "oracle",
             "sample": f"oracle gemv (DQ scale decode + dequantize + float64 matmul) over the first "
-                      f"{rows} of {N} output rows, {passes} passes in {t:.1f} s on one thread; "
-                      f"bytes per row counted as for the GPU kernel"}
+                      f"{rows} of {N} output rows, {passes} passes in {t_gemv:.1f} s; elementwise steps on one "
+                      f"thread, matmuls on {blas} BLAS threads; bytes per row counted as for the GPU kernel",
+            "ops": ops}
+
+
+def _copies(t, n):
+    """n copies of t in one allocation, as views, each starting on a 256-byte
+    boundary (the entry points refuse operands that are not 16-byte aligned)."""
+    flat = t.reshape(-1)
+    k = flat.numel()
+    per = 256 // flat.element_size()
+    stride = -(-k // per) * per
+    big = flat.new_empty(n * stride)
+    views = [big[i * stride:i * stride + k] for i in range(n)]
+    for v in views:
+        v.copy_(flat)
+    return views
+
+
+def _auto_timed(fn, stream, torch, target_us=30000.0, lo=20, hi=600):
+    """Average microseconds per call of fn(i): a short trial sizes the loop
+    to about target_us of GPU time.  fn returns the entry point's status,
+    checked on the warm-up calls."""
+    for i in range(3):
+        _ok(fn(i))
+    trial = timed_loop(fn, 8, stream, torch)
+    iters = int(min(hi, max(lo, target_us / max(trial, 1e-3))))
+    return timed_loop(fn, iters, stream, torch), iters
+
+
+def _ok(rc):
+    if rc != 0:
+        from quantized_matvec_amd import qmv
+        raise RuntimeError(f"entry point failed: {rc} ({qmv._status_string(rc)})")
+
+
+def config_rows(torch, dev, stream, ceil):
+    """Every workload of the parity suite, timed on the device: for each
+    weight and quant type, quantize (with double quantization where the
+    workload has it), dequantize to the weight's dtype and gemv / gemm at the
+    workload's row counts.  Each op rotates over distinct copies of its
+    operands (> 512 MB per rotation, twice the Infinity Cache) so the bytes
+    come from HBM, and is timed with HIP events on the launch stream."""
+    from quantized_matvec_amd import qmv, synth
+    L = qmv.lib()
+    s_h = stream.cuda_stream
+    rows = []
+    code = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    qcode = {"nf4": 0, "fp4": 1}
+    read, copy = ceil["read_gbs"], ceil["copy_gbs"]
+    extra_m = {4: (1, 8), 5: (1, 2, 4, 8)}
+    gemm_m = {4: (8, 32, 128, 512, 1024, 2048)}
+    for cfg in (1, 2, 3, 4, 5):
+        wl = synth.WORKLOADS[cfg]
+        for which, (Nw, Kw) in enumerate(wl.weights):
+            W0 = synth.weight(cfg, which).to(dev)
+            numel, wb = Nw * Kw, W0.element_size()
+            bs, dq = wl.blocksize, wl.double_quant
+            nb = numel // bs
+            st_bytes = (nb + 4 * (-(-nb // BS2)) + 4 + 4 * 256) if dq else 4 * nb
+            n_w = max(2, -(-ROTATE_BYTES // (numel * wb)))
+            n_p = max(2, -(-ROTATE_BYTES // (numel // 2)))
+            Ws = _copies(W0, n_w)
+            wout = _copies(torch.empty_like(W0), n_w)
+            for qt in wl.quant_types:
+                tag = {"cfg": f"c{cfg}", "weight": f"{Nw}x{Kw}", "w_dtype": wl.w_dtype, "quant_type": qt,
+                       "blocksize": bs, "double_quant": dq}
+                p0, st0 = qmv.quantize_4bit(W0, bs, qt, double_quant=dq, blocksize2=BS2)
+                packs = _copies(p0, n_p)
+                if dq:
+                    parts = [_copies(t, n_p) for t in (st0.absmax_q, st0.absmax2, st0.offset, st0.code2)]
+                    states = [qmv.QuantState(st0.shape, st0.dtype, bs, qt, None, *[p[i] for p in parts], BS2)
+                              for i in range(n_p)]
+                else:
+                    states = [qmv.QuantState(st0.shape, st0.dtype, bs, qt, a)
+                              for a in _copies(st0.absmax, n_p)]
+                cs = [st._c() for st in states]
+                refs = [ctypes.byref(c) for c in cs]
+                pp = [p.data_ptr() for p in packs]
+
+                def add(op, us, iters, nbytes, ceiling, m=None, flops=None):
+                    r = dict(tag, op=op, us=round(us, 3), launches_timed=iters, bytes=nbytes,
+                             gbs=round(nbytes / us / 1e3, 1), hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4))
+                    if m is not None:
+                        r["M"] = m
+                    if ceiling:
+                        r["ceiling"] = ceiling
+                        r["ceiling_frac"] = round(nbytes / us / 1e3 / (read if ceiling == "read" else copy), 4)
+                    if flops is not None:
+                        r.update(flops=flops, tflops=round(flops / us / 1e6, 2),
+                                 mfma_frac=round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4))
+                    rows.append(r)
+
+                # quantize (+ double quantization) into rotating outputs
+                qb = _copies(torch.empty_like(p0), n_w)
+                ab = _copies(torch.empty(nb, dtype=torch.float32, device=dev), n_w)
+                if dq:
+                    dqo = [_copies(t, n_w) for t in (torch.empty_like(st0.absmax_q), torch.empty_like(st0.absmax2),
+                                                     torch.empty_like(st0.offset), torch.empty_like(st0.code2))]
+                    ws = torch.zeros(max(16, L.qmv_double_quant_workspace(nb, BS2)), dtype=torch.uint8, device=dev)
+
+                def run_q(i):
+                    j = i % n_w
+                    rc = L.qmv_quantize_4bit(Ws[j].data_ptr(), code[W0.dtype], numel, bs, qcode[qt],
+                                             qb[j].data_ptr(), ab[j].data_ptr(), s_h)
+                    if dq and rc == 0:
+                        rc = L.qmv_double_quant(ab[j].data_ptr(), nb, BS2, None, dqo[0][j].data_ptr(),
+                                                dqo[1][j].data_ptr(), dqo[2][j].data_ptr(), dqo[3][j].data_ptr(),
+                                                ws.data_ptr(), ws.numel(), s_h)
+                    return rc
+
+                us, it = _auto_timed(run_q, stream, torch)
+                add("quantize_4bit+double_quant" if dq else "quantize_4bit", us, it,
+                    wb * numel + numel // 2 + st_bytes, "copy")
+
+                def run_d(i):
+                    return L.qmv_dequantize_4bit(pp[i % n_p], refs[i % n_p], numel, bs, qcode[qt],
+                                          wout[i % n_w].data_ptr(), code[W0.dtype], s_h)
+
+                us, it = _auto_timed(run_d, stream, torch)
+                add("dequantize_4bit", us, it, numel // 2 + st_bytes + wb * numel, "copy")
+
+                xfull = synth.activations(cfg, which).to(dev)
+                xdt = xfull.dtype
+                for m in extra_m.get(cfg, wl.ms):
+                    x = xfull[:m].contiguous()
+                    y = torch.empty(m, Nw, dtype=xdt, device=dev)
+
+                    def run_v(i, x=x, y=y, m=m):
+                        return L.qmv_gemv_4bit(x.data_ptr(), code[xdt], m, Nw, Kw, pp[i % n_p], refs[i % n_p], bs,
+                                        qcode[qt], y.data_ptr(), code[xdt], None, s_h)
+
+                    us, it = _auto_timed(run_v, stream, torch)
+                    add("gemv_4bit", us, it, numel // 2 + st_bytes + x.element_size() * m * (Kw + Nw), "read", m=m)
+                for m in gemm_m.get(cfg, ()):
+                    A = (xfull[:m] if m <= xfull.shape[0] else
+                         synth.gaussian((m, Kw), 1.0, 100 * cfg + 7, wl.x_dtype)).contiguous().to(dev)
+                    C = torch.empty(m, Nw, dtype=xdt, device=dev)
+
+                    def run_g(i, A=A, C=C, m=m):
+                        return L.qmv_gemm_4bit(A.data_ptr(), code[xdt], m, Nw, Kw, pp[i % n_p], refs[i % n_p], bs,
+                                        qcode[qt], C.data_ptr(), code[xdt], None, s_h)
+
+                    us, it = _auto_timed(run_g, stream, torch, hi=200)
+                    add("gemm_4bit", us, it, numel // 2 + st_bytes + A.element_size() * m * (Kw + Nw), None,
+                        m=m, flops=2.0 * m * Nw * Kw)
+                    del A, C
+                torch.cuda.synchronize()
+                print(f"[bench] c{cfg} {Nw}x{Kw} {qt} timed", file=sys.stderr, flush=True)
+                del packs, states, cs, refs, qb, ab
+            del Ws, wout, W0
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    return rows
 
 
 COPY_BYTES = 1 << 30
@@ -147,15 +339,17 @@ COPY_BYTES = 1 << 30
 
 def measured_ceilings(torch, dev, reps=20):
     """Streaming ceilings of this GPU, to read the kernels' GB/s against: a
-    plain 128-bit read of 1 GiB (the library's stream_read probe) and torch's
-    device copy of 1 GiB (bytes read + written).  Event-timed on torch's
-    current stream, the probe's launch stream, after two warm-up passes."""
+    plain 128-bit read of 1 GiB (the library's stream_read probe), torch's
+    fill of 1 GiB (write only) and torch's device copy of 1 GiB (bytes read +
+    written).  Event-timed on torch's current stream, the probe's launch
+    stream, after two warm-up passes."""
     from quantized_matvec_amd import qmv
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
     out = {}
     for name, fn, nbytes in (("read_gbs", lambda: qmv.stream_read(src, sink), COPY_BYTES),
+                             ("write_gbs", lambda: dst.fill_(1.0), COPY_BYTES),
                              ("copy_gbs", lambda: dst.copy_(src), 2 * COPY_BYTES)):
         for _ in range(2):
             fn()
@@ -169,9 +363,33 @@ def measured_ceilings(torch, dev, reps=20):
         us = a.elapsed_time(b) / reps * 1e3
         out[name] = round(nbytes / us / 1e3, 1)
     del src, dst
-    out["method"] = ("stream_read probe over 1 GiB (128-bit loads, grid-stride) and torch copy_ of 1 GiB "
-                     "(bytes read + written), event-timed")
+    out["method"] = ("stream_read probe over 1 GiB (128-bit loads, grid-stride, one sink word per "
+                     "workgroup), torch fill_ of 1 GiB (written bytes) and torch copy_ of 1 GiB (bytes "
+                     "read + written), event-timed")
     return out
+
+
+def clocks():
+    """Current GPU clocks as the driver reports them (best effort)."""
+    import glob
+    import subprocess
+    out = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[:1] + \
+            sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_mclk"))[:1]:
+        try:
+            with open(path) as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            out[os.path.basename(path)] = cur[0] if cur else None
+        except OSError:
+            pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [ln.strip() for ln in r.stdout.splitlines() if "clock level" in ln.lower() or "Mhz" in ln]
+        if lines:
+            out["rocm_smi"] = lines[:8]
+    except Exception:  # noqa: BLE001 - informational only
+        pass
+    return out or None
 
 
 def host_info():
@@ -219,6 +437,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (every weight, quant type and row count)")
     ap.add_argument("--counters", choices=["gemv_4bit", "gemm_4bit", "dequantize_4bit", "quantize_4bit"],
                     help="for hardware-counter runs: one 1 GiB copy (the calibration kernel), "
                          "then 10 launches of the named kernel over distinct weight copies")
@@ -297,22 +517,22 @@ def main():
         w_ptr = [w.data_ptr() for w in wout]
 
         def run_gemv(i):
-            L.qmv_gemv_4bit(x_ptr, 2, M_GEMV, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, y_ptr, 2, None,
-                            s_h)
+            return L.qmv_gemv_4bit(x_ptr, 2, M_GEMV, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, y_ptr, 2, None,
+                                   s_h)
 
         def run_gemm(i):
-            L.qmv_gemm_4bit(A_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, C_ptr, 2, None,
-                            s_h)
+            return L.qmv_gemm_4bit(A_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0, C_ptr, 2, None,
+                                   s_h)
 
         def run_deq(i):
-            L.qmv_dequantize_4bit(p_ptr[i % n_p], scs[i % n_p], N * K, BS, 0, w_ptr[i % n_w], 2, s_h)
+            return L.qmv_dequantize_4bit(p_ptr[i % n_p], scs[i % n_p], N * K, BS, 0, w_ptr[i % n_w], 2, s_h)
 
         qbuf = [torch.empty_like(packed0) for _ in range(n_w)]
         abuf = [torch.empty_like(st0.absmax_q, dtype=torch.float32) for _ in range(n_w)]
 
         def run_quant(i):      # the raw entry point (no allocation inside the loop)
-            L.qmv_quantize_4bit(Ws[i % n_w].data_ptr(), 2, N * K, BS, 0, qbuf[i % n_w].data_ptr(),
-                                abuf[i % n_w].data_ptr(), s_h)
+            return L.qmv_quantize_4bit(Ws[i % n_w].data_ptr(), 2, N * K, BS, 0, qbuf[i % n_w].data_ptr(),
+                                       abuf[i % n_w].data_ptr(), s_h)
 
         dq_out = [(torch.empty_like(st0.absmax_q), torch.empty_like(st0.absmax2),
                    torch.empty_like(st0.offset), torch.empty_like(st0.code2)) for _ in range(n_w)]
@@ -321,8 +541,8 @@ def main():
 
         def run_dq(i):
             q, a2, off, c2 = dq_out[i % n_w]
-            L.qmv_double_quant(abuf[i % n_w].data_ptr(), nbk, BS2, None, q.data_ptr(), a2.data_ptr(),
-                               off.data_ptr(), c2.data_ptr(), ws.data_ptr(), ws.numel(), s_h)
+            return L.qmv_double_quant(abuf[i % n_w].data_ptr(), nbk, BS2, None, q.data_ptr(), a2.data_ptr(),
+                                      off.data_ptr(), c2.data_ptr(), ws.data_ptr(), ws.numel(), s_h)
 
         # gemm_4bit_backward (dX = dY @ W_hat) on the same weight, dY [512, 14336]
         dY = synth.gaussian((M_GEMM, N), 1.0, 100 * 4 + 3, "bf16").to(dev)
@@ -330,8 +550,8 @@ def main():
         dY_ptr, dX_ptr = dY.data_ptr(), dX.data_ptr()
 
         def run_bwd(i):
-            L.qmv_gemm_4bit_backward(dY_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0,
-                                     dX_ptr, 2, s_h)
+            return L.qmv_gemm_4bit_backward(dY_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0,
+                                            dX_ptr, 2, s_h)
 
         # the 8-bit blockwise codec on the same bf16 weights (blocksize 4096),
         # with the default linear table and with the dynamic-tree table
@@ -341,12 +561,12 @@ def main():
         tree_p = ctypes.cast(tree, ctypes.c_void_p)
 
         def run_q8(i, code=None):
-            L.qmv_quantize_blockwise(Ws[i % n_w].data_ptr(), 2, N * K, BS8, code, q8[i % n_w].data_ptr(),
-                                     a8[i % n_w].data_ptr(), s_h)
+            return L.qmv_quantize_blockwise(Ws[i % n_w].data_ptr(), 2, N * K, BS8, code, q8[i % n_w].data_ptr(),
+                                            a8[i % n_w].data_ptr(), s_h)
 
         def run_dq8(i):
-            L.qmv_dequantize_blockwise(q8[i % n_w].data_ptr(), a8[i % n_w].data_ptr(), N * K, BS8, None,
-                                       w_ptr[i % n_w], 2, s_h)
+            return L.qmv_dequantize_blockwise(q8[i % n_w].data_ptr(), a8[i % n_w].data_ptr(), N * K, BS8, None,
+                                              w_ptr[i % n_w], 2, s_h)
 
         # embedding_4bit: EMB_T random rows of a [EMB_V, K] NF4 table (block 64,
         # double-quantized scales) to bf16
@@ -360,8 +580,8 @@ def main():
         ec = ste._c()
 
         def run_emb(i):
-            L.qmv_embedding_4bit(eidx.data_ptr(), EMB_T, EMB_V, K, pe.data_ptr(), ctypes.byref(ec), BS, 0,
-                                 eout.data_ptr(), 2, s_h)
+            return L.qmv_embedding_4bit(eidx.data_ptr(), EMB_T, EMB_V, K, pe.data_ptr(), ctypes.byref(ec), BS, 0,
+                                        eout.data_ptr(), 2, s_h)
 
         for name, fn, iters in (("gemv_4bit", run_gemv, kiters), ("gemm_4bit", run_gemm, kiters // 4),
                                 ("gemm_4bit_backward", run_bwd, kiters // 8),
@@ -373,7 +593,7 @@ def main():
                                 ("dequantize_blockwise", run_dq8, kiters // 4),
                                 ("embedding_4bit", run_emb, kiters // 4)):
             for i in range(5):
-                fn(i)
+                _ok(fn(i))
             kern[name] = timed_loop(fn, iters, stream, torch)
 
     rep = {}
@@ -425,9 +645,13 @@ def main():
                 "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
         "kernels": rep,
         "step_wall_ms": round(wall_step_ms, 4),
+        "clocks": clocks(),
     }
+    if not args.no_configs:
+        with torch.cuda.stream(stream):
+            out["configs"] = config_rows(torch, dev, stream, ceil)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(W_cpu, x_cpu)
+        out["cpu_baseline"] = cpu_baseline(W_cpu, x_cpu, A_cpu)
         out["cpu_baseline"]["host"] = host_info()
     print(json.dumps(out), flush=True)
 

@@ -16,14 +16,16 @@ extern "C" {
 
 /*
  * stream_read: reads every byte of p once with 128-bit loads (a grid-stride
- * pass over the whole buffer) and XORs all of its 32-bit words into *sink, so
- * the reads cannot be elided; timed over a buffer much larger than the
- * caches it gives the streaming-read ceiling.
+ * pass over the whole buffer by at most 1024 workgroups) and XORs the 32-bit
+ * words each workgroup read into its own word of sink, so the reads cannot
+ * be elided and no two workgroups touch one address; timed over a buffer
+ * much larger than the caches it gives the streaming-read ceiling.  The XOR
+ * of the 1024 sink words is the XOR of every word of p.
  *   p       device, 16-byte aligned (QMV_ERR_ALIGNMENT), bytes > 0 and a
  *           multiple of 16 (QMV_ERR_INVALID_ARG)
- *   sink    device uint32, 4-byte aligned; XORed into, not cleared: the
- *           caller zeroes it to read the checksum.  Concurrent calls on one
- *           sink race.
+ *   sink    device uint32 [1024], 4-byte aligned; XORed into, not cleared:
+ *           the caller zeroes it to read the checksum.  Concurrent calls on
+ *           one sink race.
  *   stream  hipStream_t; the call only enqueues.
  * Returns QMV_OK or an error status of qmv.h.
  */

@@ -8,12 +8,16 @@ namespace qmv {
 
 constexpr int kProbeThreads = 256;
 
+constexpr int kProbeMaxGrid = 1024;  // workgroups, one sink word each
+
 // Every 16-byte chunk is read once (grid-stride, consecutive lanes on
-// consecutive chunks); a wave XORs its words together and one lane folds
-// the result into *sink with an atomic, so the loads cannot be dropped.
+// consecutive chunks); the workgroup XORs its words together and XORs the
+// result into its own sink word (a plain read-modify-write: no atomics, which
+// would serialise on one address at the end of the pass).
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4 *__restrict__ p,
                                                                     int64_t n16,
                                                                     uint32_t *__restrict__ sink) {
+  __shared__ uint32_t part[kProbeThreads / 64];
   uint32_t acc = 0;
   const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
   for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) {
@@ -22,12 +26,18 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4 
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, d);
-  if ((threadIdx.x & 63) == 0 && acc != 0) atomicXor(sink, acc);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t w = 0;
+    for (int i = 0; i < kProbeThreads / 64; ++i) w ^= part[i];
+    sink[blockIdx.x] ^= w;
+  }
 }
 
 hipError_t launch_stream_read(const void *p, int64_t bytes, uint32_t *sink, hipStream_t st) {
   const int64_t n16 = bytes / 16;
-  int64_t grid = 4 * (int64_t)device_cu_count();
+  int64_t grid = std::min<int64_t>(4 * (int64_t)device_cu_count(), kProbeMaxGrid);
   grid = std::min<int64_t>(grid, (n16 + kProbeThreads - 1) / kProbeThreads);
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, st,
                      static_cast<const uint4 *>(p), n16, sink);
