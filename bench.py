@@ -439,7 +439,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload table (every weight, quant type and row count)")
-    ap.add_argument("--counters", choices=["gemv_4bit", "gemm_4bit", "dequantize_4bit", "quantize_4bit"],
+    ap.add_argument("--counters", choices=["gemv_4bit", "gemm_4bit", "gemm_4bit_backward", "dequantize_4bit",
+                                           "quantize_4bit", "double_quant"],
                     help="for hardware-counter runs: one 1 GiB copy (the calibration kernel), "
                          "then 10 launches of the named kernel over distinct weight copies")
     args = ap.parse_args()
@@ -468,6 +469,7 @@ def main():
         x = x_cpu.to(dev)
         A = A_cpu.to(dev)
         packed0, st0 = qmv.quantize_4bit(W, BS, "nf4", double_quant=True, blocksize2=BS2)
+        _, st0_plain = qmv.quantize_4bit(W, BS, "nf4")
         # distinct copies so repeated launches stream from HBM, not the cache
         n_w = max(2, -(-ROTATE_BYTES // (W.numel() * 2)))
         n_p = max(2, -(-ROTATE_BYTES // packed0.numel()))
@@ -488,8 +490,13 @@ def main():
             qmv.gemm_4bit(A, p, st, out=C)
 
         if args.counters:
+            dY0 = synth.gaussian((M_GEMM, N), 1.0, 100 * 4 + 3, "bf16").to(dev)
+            dX0 = torch.empty(M_GEMM, K, dtype=torch.bfloat16, device=dev)
             counters_run(args.counters, dict(gemv_4bit=lambda i: qmv.gemv_4bit(x, packs[i], states[i], out=y),
                                              gemm_4bit=lambda i: qmv.gemm_4bit(A, packs[i], states[i], out=C),
+                                             gemm_4bit_backward=lambda i: qmv.gemm_4bit_backward(
+                                                 dY0, packs[i], states[i], out=dX0),
+                                             double_quant=lambda i: qmv.double_quant(st0_plain.absmax),
                                              dequantize_4bit=lambda i: qmv.dequantize_4bit(
                                                  packs[i], states[i], out=wout[i % n_w]),
                                              quantize_4bit=lambda i: qmv.quantize_4bit(
