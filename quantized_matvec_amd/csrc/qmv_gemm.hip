@@ -782,8 +782,9 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_f32_kernel(const float *__re
 // v_mfma_f32_32x32x16_bf16 (f16), one wave per SIMD.  Per k-tile of 64:
 //  * the activations go global -> LDS with 16-byte LDS-direct loads into a
 //    3-stage ring (128 rows x 128 B per stage; a row's 16-byte chunks are
-//    XOR-swizzled by row % 8, so the MFMA operand reads of 32 rows spread
-//    over all banks), issued two k-tiles ahead;
+//    XOR-swizzled by (row / 2) % 8: two 128-byte rows share one 256-byte
+//    sweep of the banks, so 16 consecutive rows read at one chunk position
+//    land on 16 different 16-byte bank groups), issued two k-tiles ahead;
 //  * each wave decodes its own weights straight into MFMA operand registers
 //    (no LDS tile for the weights): lane l covers column 32 j + l % 32 and the
 //    32 k-values 32 (l / 32) .. + 31 (one 16-byte packed load), so MFMA t
@@ -858,7 +859,7 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
     offset = sc.offset[0];
   }
   // activations: wave w moves rows (4 w + d) * 8 + l / 8 of a stage, lane l
-  // into position l % 8 of its row, from chunk (l % 8) ^ (row % 8); rows
+  // into position l % 8 of its row, from chunk (l % 8) ^ ((row / 2) % 8); rows
   // past M read zeros (bounded resource)
   const int64_t mrows = M - m0 < kRbM ? M - m0 : kRbM;
   const uint16_t *a_base = A + m0 * K;
@@ -867,7 +868,7 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int r = (4 * wave + d) * 8 + (lane >> 3);
-    aoff[d] = (uint32_t)(r * K * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+    aoff[d] = (uint32_t)(r * K * 2) + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
   auto issue_a = [&](int kt, uint4 *stage) {  // k-tiles past the end re-read the last one
     const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * (kRbK * 2);
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 32 * i + colw;
-        af[i] = __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ (r & 7))]);
+        af[i] = __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ ((r >> 1) & 7))]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
