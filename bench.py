@@ -555,10 +555,12 @@ def main():
         dY = synth.gaussian((M_GEMM, N), 1.0, 100 * 4 + 3, "bf16").to(dev)
         dX = torch.empty(M_GEMM, K, dtype=torch.bfloat16, device=dev)
         dY_ptr, dX_ptr = dY.data_ptr(), dX.data_ptr()
+        bws_n = L.qmv_gemm_4bit_backward_workspace(M_GEMM, N, K, BS)
+        bws = torch.empty(max(bws_n, 256), dtype=torch.uint8, device=dev)
 
         def run_bwd(i):
             return L.qmv_gemm_4bit_backward(dY_ptr, 2, M_GEMM, N, K, p_ptr[i % n_p], scs[i % n_p], BS, 0,
-                                            dX_ptr, 2, s_h)
+                                            dX_ptr, 2, bws.data_ptr(), bws.numel(), s_h)
 
         # the 8-bit blockwise codec on the same bf16 weights (blocksize 4096),
         # with the default linear table and with the dynamic-tree table

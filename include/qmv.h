@@ -51,7 +51,7 @@ typedef enum {
   QMV_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned */
   QMV_ERR_LAUNCH = -4,      /* the HIP runtime refused a kernel launch */
   QMV_ERR_HIP = -5,         /* another HIP runtime call failed */
-  QMV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than qmv_double_quant_workspace() */
+  QMV_ERR_WORKSPACE = -6,   /* workspace missing, misaligned or smaller than its size query */
   QMV_ERR_TOO_LARGE = -7    /* more scales than qmv_double_quant_noalloc's fixed scratch holds */
 } qmv_status;
 
@@ -222,16 +222,25 @@ int qmv_dequantize_blockwise(const uint8_t *q, const float *absmax, int64_t n, i
  *   dX[m, k] = sum_n dY[m, n] * W_hat[n, k], fp32 accumulation.
  *   dY [M, N] device row-major bf16 or fp16;  dX [M, K] device row-major, dx_dtype
  *   W_hat [N, K] as for gemm_4bit (the same packed codes and scales).
- * The weight is dequantized tile by tile into LDS exactly as by
- * dequantize_4bit to dY's type and multiplied on the matrix cores in that
- * type.  No bias: the backward has no epilogue.
+ * The weight is dequantized tile by tile exactly as by dequantize_4bit to
+ * dY's type and multiplied on the matrix cores in that type.  No bias: the
+ * backward has no epilogue.
+ *   workspace  device scratch of at least qmv_gemm_4bit_backward_workspace(M,
+ *              N, K, blocksize) bytes, 16-byte aligned, any contents (NULL
+ *              when that is 0; QMV_ERR_WORKSPACE when missing or smaller).
+ *              When the reduction over N is split across workgroups it holds
+ *              one counter per output tile, which the call zeroes on its
+ *              stream first, and the fp32 partial tiles.  Calls that share a
+ *              workspace must not overlap.
  * Requires dy_dtype bf16 or fp16, N % 32 == 0, K % blocksize == 0 and
  * K % 32 == 0, else QMV_ERR_UNSUPPORTED.  Buffers are the caller's; dX is
  * fully overwritten.
  */
+size_t qmv_gemm_4bit_backward_workspace(int64_t M, int64_t N, int64_t K, int32_t blocksize);
 int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_t N, int64_t K,
                            const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
-                           qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *stream);
+                           qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * embedding_4bit: rows of a 4-bit quantized embedding table

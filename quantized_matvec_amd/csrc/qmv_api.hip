@@ -303,9 +303,15 @@ int qmv_gemm_4bit(const void *A, qmv_dtype a_dtype, int64_t M, int64_t N, int64_
                                         quant_type, C, c_dtype, bias, (hipStream_t)stream));
 }
 
+size_t qmv_gemm_4bit_backward_workspace(int64_t M, int64_t N, int64_t K, int32_t blocksize) {
+  if (check_matmul(M, N, K, blocksize, QMV_NF4) != QMV_OK) return 0;
+  return gemm_backward_workspace_bytes(M, N, K, log2_exact(blocksize));
+}
+
 int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_t N, int64_t K,
                            const uint8_t *packed, const qmv_absmax *scales, int32_t blocksize,
-                           qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *stream) {
+                           qmv_quant_type quant_type, void *dX, qmv_dtype dx_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   if (!dY || !packed || !dX || !valid_dtype(dy_dtype) || !valid_dtype(dx_dtype))
     return QMV_ERR_INVALID_ARG;
   int rc = check_matmul(M, N, K, blocksize, quant_type);
@@ -317,8 +323,10 @@ int qmv_gemm_4bit_backward(const void *dY, qmv_dtype dy_dtype, int64_t M, int64_
   rc = check_scales(scales, &sc, &dq);
   if (rc != QMV_OK) return rc;
   if (!aligned16(dY) || !aligned16(packed) || !aligned16(dX)) return QMV_ERR_ALIGNMENT;
+  const size_t need = gemm_backward_workspace_bytes(M, N, K, log2_exact(blocksize));
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return QMV_ERR_WORKSPACE;
   return launch_status(launch_gemm_4bit_backward(dY, dy_dtype, M, N, K, packed, sc, dq, log2_exact(blocksize),
-                                                 quant_type, dX, dx_dtype, (hipStream_t)stream));
+                                                 quant_type, dX, dx_dtype, workspace, (hipStream_t)stream));
 }
 
 int qmv_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64_t D, const uint8_t *packed,

@@ -1173,6 +1173,335 @@ hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, in
 }
 
 // ---------------------------------------------------------------------------
+// gemm_4bit_backward, register-free transpose: gemm_4bit_dxt_kernel
+//
+// dX[M, K] = dY[M, N] @ W_hat[N, K] with the reduction over N, whose packed
+// rows run along K: the weight tile has to be turned around before the
+// matrix cores can take it as their B operand (8 consecutive reduction
+// values n per lane).  A workgroup of 4 waves owns a 128 (M) x 256 (K) tile
+// of dX and a contiguous range of reduction steps of 64 rows of W; wave w
+// computes all 128 rows x columns [64 w, 64 w + 64) as 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16 (f16).  Per step:
+//  * dY's 128 x 64 tile goes global -> LDS through 16-byte LDS-direct loads
+//    into a 3-stage ring issued two steps ahead (the forward large-M
+//    kernel's activation ring, with n in place of k);
+//  * lane l of wave w decodes row n0 + l of the step, columns [64 w, + 64):
+//    two 16-byte packed loads, one block scale (blocks >= 64 columns), 32
+//    lookups of the fp32 pair table, fp32(T * a_hat) rounded to dY's type
+//    -- exactly the dequantize_4bit values -- and writes the 128-byte row
+//    into the wave's own 64 x 64 LDS block (no other wave reads it, so no
+//    barrier guards it);
+//  * the B operand comes back out of that block with ds_read_b64_tr_b16:
+//    within each 16 lanes the instruction returns, to lane i, element i % 4
+//    of what lanes 4 e + i / 4 (e = 0..3) addressed, so lanes that address 4
+//    consecutive rows x 4 consecutive columns hand every lane one column's 4
+//    rows.  Two such reads give a lane the 8 reduction values of its column.
+//    The block's 16-byte chunks are XOR-swizzled by g(n) = ((j & 1) << 2) |
+//    (j >> 1), j = (n / 2) % 8, which keeps both the row writes (16 rows,
+//    one chunk position) and the transposed reads (4 rows x 8 eight-byte
+//    units) on distinct banks.
+// When 128 x 256 tiles would leave compute units idle, the reduction is split
+// over S workgroups per tile: each writes its fp32 partial tile to the
+// workspace and bumps the tile's counter; the workgroup that finds the count
+// complete adds the S partials in split order (the same sum whichever
+// finishes last) and stores dX.  A one-block launch zeroes the counters
+// first (a workspace that served another shape may hold partials where the
+// counters are now).  The workgroups of a
+// tile run on different XCDs, whose L2 caches are not coherent with each
+// other for ordinary accesses: the partials and the counter are written and
+// read with agent-scope atomic accesses, which bypass the non-coherent
+// caches.
+// ---------------------------------------------------------------------------
+constexpr int kDxM = 128, kDxK = 256, kDxN = 64;
+
+__device__ __forceinline__ int dxt_swz(int n) {  // 16-byte chunk swizzle of weight row n
+  const int j = (n >> 1) & 7;
+  return ((j & 1) << 2) | (j >> 1);
+}
+
+template <int ADT, int CDT, bool DQ>
+__global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
+    const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
+    Scales sc, int log2bs, Table16f table, void *__restrict__ dXv, int ktiles, int splits, int steps_per_split,
+    float *__restrict__ part, uint32_t *__restrict__ counters) {
+  using CT = typename Storage<CDT>::type;
+  CT *dX = static_cast<CT *>(dXv);
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 32 * 2];  // byte -> (T[hi], T[lo]), 32 copies
+  __shared__ float code2[256];
+  __shared__ uint4 st0[kDxM * 8], st1[kDxM * 8], st2[kDxM * 8];       // dY ring
+  __shared__ __attribute__((aligned(16))) uint4 wbuf[4 * kDxN * 8];  // decoded weights, 8 KB per wave
+  __shared__ int last_flag;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = (int)blockIdx.x % splits;
+  const int tile = (int)blockIdx.x / splits;
+  const int64_t m0 = (int64_t)(tile / ktiles) * kDxM;
+  const int64_t k0 = (int64_t)(tile % ktiles) * kDxK;
+  const int NT = (int)(N / kDxN);
+  const int nt0 = s * steps_per_split;
+  const int nsteps = NT - nt0 < steps_per_split ? NT - nt0 : steps_per_split;  // >= 1
+  {  // table: 16-byte chunk c holds copies 2 (c % 16) and + 1 of entry c / 16
+    const uint32_t lo = __float_as_uint(table.v[(tid >> 4) & 15]);
+    uint4 *dst = reinterpret_cast<uint4 *>(lut);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const uint32_t hi = __float_as_uint(table.v[it]);
+      dst[it * 256 + tid] = make_uint4(hi, lo, hi, lo);
+    }
+  }
+  float offset = 0.f;
+  if constexpr (DQ) {
+    code2[tid] = sc.code2[tid];
+    offset = sc.offset[0];
+  }
+  // dY: wave w moves rows (4 w + d) * 8 + l / 8 of a stage, lane l into
+  // position l % 8 of its row, from chunk (l % 8) ^ ((row / 2) % 8); rows past
+  // M read zeros (bounded resource)
+  const int64_t mrows = M - m0 < kDxM ? M - m0 : kDxM;
+  const uint16_t *a_base = dY + m0 * N;
+  const uint32_t a_bytes = (uint32_t)(mrows * N * 2);
+  uint32_t aoff[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int r = (4 * wave + d) * 8 + (lane >> 3);
+    aoff[d] = (uint32_t)(r * N * 2) + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+  }
+  auto issue_a = [&](int l, uint4 *stage) {  // step l of this split; steps past the end re-read the last
+    const uint32_t no = (uint32_t)(nt0 + (l < nsteps ? l : nsteps - 1)) * (kDxN * 2);
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc_u(a_base, a_bytes);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) load_lds16(ars, stage + (4 * wave + d) * 64, aoff[d] + no);
+  };
+  // weights: lane l -> row n0 + l of the step, columns k0 + 64 w .. + 63 (32 bytes, one block)
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const int64_t kcol = k0 + 64 * wave;
+  const int64_t bpr = K >> log2bs;  // blocks per weight row
+  struct BR {
+    uint4 w[2];
+    uint32_t q;
+    float s;
+  };
+  auto issue_b = [&](int l, BR &b) {
+    const int64_t row0 = (int64_t)(nt0 + (l < nsteps ? l : nsteps - 1)) * kDxN;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc_u(packed + row0 * rowb, kDxN * rowb);
+    const uint32_t off = (uint32_t)lane * rowb + (uint32_t)(kcol >> 1);
+    b.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0));
+    b.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, 0));
+    const int64_t blk = (row0 + lane) * bpr + (kcol >> log2bs);
+    if constexpr (DQ) {
+      b.q = sc.q[blk];
+      b.s = sc.absmax2[blk >> sc.log2bs2];
+    } else {
+      b.s = sc.absmax[blk];
+    }
+  };
+  issue_a(0, st0);
+  issue_a(1, st1);
+  BR br0, br1, br2;
+  issue_b(0, br0);
+  issue_b(1, br1);
+  __syncthreads();  // table and code2
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const uint32_t lane_sel = (uint32_t)(lane & 31) << 3;
+  const char *lut_b = reinterpret_cast<const char *>(lut);
+  uint4 *wmine = wbuf + wave * (kDxN * 8);
+  const int wsw = dxt_swz(lane);  // this lane's row is row `lane` of the block
+  // decode row `lane` of the step into the wave's block, chunk p (8 values,
+  // columns 8 p .. 8 p + 7) at position p ^ swizzle
+  auto decode = [&](const BR &b) __attribute__((always_inline)) {
+    const float a = DQ ? code2[b.q & 255u] * b.s + offset : b.s;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t w = (p >> 2) == 0 ? ((p & 3) == 0 ? b.w[0].x : (p & 3) == 1 ? b.w[0].y : (p & 3) == 2 ? b.w[0].z : b.w[0].w)
+                                       : ((p & 3) == 0 ? b.w[1].x : (p & 3) == 1 ? b.w[1].y : (p & 3) == 2 ? b.w[1].z : b.w[1].w);
+      float2 tv[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const uint32_t addr = __builtin_amdgcn_perm(w, lane_sel, 0x0c0c0000u | ((4u + bb) << 8));
+        tv[bb] = *reinterpret_cast<const float2 *>(lut_b + addr);
+      }
+      uint32_t o[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) o[bb] = cvt_pair<ADT>(tv[bb].x * a, tv[bb].y * a);
+      wmine[lane * 8 + (p ^ wsw)] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  // transposed B operand of MFMA step t (reduction rows 16 t + 8 h .. + 7)
+  // for column block j (columns 32 j + lane % 32): lane l addresses row
+  // 16 t + 8 h + 4 r + (l % 16) / 4 and the 4 columns starting at
+  // 32 j + 16 ((l / 16) % 2) + 4 (l % 4)
+  typedef short v4s_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+  const int h = lane >> 5, colw = lane & 31;
+  auto bfrag = [&](int t, int j) __attribute__((always_inline)) {
+    uint32_t v[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int n = 16 * t + 8 * h + 4 * r + ((lane & 15) >> 2);
+      const int u = 8 * j + 4 * ((lane >> 4) & 1) + (lane & 3);  // 8-byte unit of the row
+      const int phys = ((((u >> 1) ^ dxt_swz(n)) << 1) | (u & 1));
+      const v4s_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s_t *)(reinterpret_cast<char *>(wmine) + n * 128 + phys * 8));
+      const uint2 xx = __builtin_bit_cast(uint2, x);
+      v[2 * r] = xx.x;
+      v[2 * r + 1] = xx.y;
+    }
+    return __builtin_bit_cast(bf16x8_t, make_uint4(v[0], v[1], v[2], v[3]));
+  };
+  auto mma = [&](const uint4 *stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8_t b0 = bfrag(t, 0), b1 = bfrag(t, 1);
+      const int c = 2 * t + h;  // this lane's 16-byte chunk of the dY row for MFMA t
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + colw;
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ ((r >> 1) & 7))]);
+        acc[i][0] = mfma16<ADT>(af, b0, acc[i][0]);
+        acc[i][1] = mfma16<ADT>(af, b1, acc[i][1]);
+      }
+    }
+  };
+  // step l: dY(l) in stage l % 3, weights(l) in register set l % 3, both
+  // loaded two steps ahead (loads complete in order, so the wait for a
+  // step's weights also waits for everything issued before them: with two
+  // steps between issue and use neither the activations nor the weights and
+  // their scattered block scales stall the step)
+  auto step = [&](int l, uint4 *sa_cur, uint4 *sa_next2, BR &bcur, BR &bnext2) __attribute__((always_inline)) {
+    // dY(l) must have landed for every wave: this wave's loads issued since
+    // are W(l) and dY(l + 1), W(l + 1) (4 + 2 x (2 + 2), or 2 + 1 per W
+    // without double quantization)
+    constexpr int after = 4 + 2 * (DQ ? 4 : 3);
+    __builtin_amdgcn_s_waitcnt((after & 15) | (7 << 4) | (15 << 8) | ((after >> 4) << 14));
+    __syncthreads();  // and every wave is done with stage (l + 2) % 3
+    issue_a(l + 2, sa_next2);
+    issue_b(l + 2, bnext2);
+    decode(bcur);
+    mma(sa_cur);
+  };
+  int l = 0;
+  for (; l + 3 <= nsteps; l += 3) {
+    step(l, st0, st2, br0, br2);
+    step(l + 1, st1, st0, br1, br0);
+    step(l + 2, st2, st1, br2, br1);
+  }
+  {  // the remaining 0..2 steps (l is a multiple of 3 here)
+    const int rem = nsteps - l;
+    if (rem > 0) step(l, st0, st2, br0, br2);
+    if (rem > 1) step(l + 1, st1, st0, br1, br0);
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no LDS-direct load outlives the loop
+
+  if (splits > 1) {
+    // this split's partial tile, lane-major per wave: element e of lane l at
+    // e * 64 + l
+    float *mine = part + ((int64_t)(tile * splits + s) * 4 + wave) * (128 * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)  // agent-scope stores: coherent across the XCDs' L2 caches
+          __hip_atomic_store(mine + ((i * 2 + j) * 16 + r) * 64 + lane, acc[i][j][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    // the partial's agent-scope stores write through to the point of
+    // coherence; waiting for their completion (vmcnt(0)) in every wave
+    // before the count is bumped publishes them.  No release or acquire
+    // fence: at agent scope those write back and invalidate the whole L2 of
+    // the XCD (measured: +33 us on 512 x 14336 x 4096), and nothing else
+    // this kernel writes needs publishing.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(splits - 1);
+    __syncthreads();
+    if (!last_flag) return;  // the partials are read below with agent-scope (coherent) loads
+    // the S partials added in split order, 64 elements at a time with all
+    // of a split's loads in flight together
+    const float *base = part + (int64_t)tile * splits * 4 * (128 * 64) + wave * (128 * 64) + lane;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float sum[64];
+      for (int s2 = 0; s2 < splits; ++s2) {
+        float v[64];
+        if (s2 == s) {
+#pragma unroll
+          for (int e = 0; e < 64; ++e) v[e] = acc[(64 * half + e) >> 5][((64 * half + e) >> 4) & 1][e & 15];
+        } else {
+          const float *src = base + (int64_t)s2 * 4 * (128 * 64) + (64 * half) * 64;
+#pragma unroll
+          for (int e = 0; e < 64; ++e)
+            v[e] = __hip_atomic_load(src + e * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int e = 0; e < 64; ++e) sum[e] = s2 == 0 ? v[e] : sum[e] + v[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 64; ++e) acc[(64 * half + e) >> 5][((64 * half + e) >> 4) & 1][e & 15] = sum[e];
+    }
+  }
+
+  // 32 x 32 accumulator layout: column = lane % 32, row = 8 (r / 4) + 4 (lane / 32) + r % 4
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = kcol + 32 * j + colw;  // < K: K % 256 == 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < M) store_elem<CDT>(dX, row * K + col, acc[i][j][r]);
+      }
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t *__restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+// Launch shape of gemm_4bit_dxt_kernel: column tiles, splits of the
+// reduction and steps per split, and the workspace it needs (tile counters,
+// then fp32 partial tiles).  Eligible: N % 64 == 0, K % 256 == 0, blocks of
+// at least 64 columns (so a wave's 64 columns of a row lie in one block).
+struct DxtPlan {
+  bool ok;
+  int ktiles, mtiles, splits, steps;
+  size_t counter_bytes, bytes;
+};
+
+DxtPlan dxt_plan(int64_t M, int64_t N, int64_t K, int log2bs) {
+  DxtPlan p{};
+  if (N % kDxN != 0 || K % kDxK != 0 || log2bs < 6 || N >= ((int64_t)1 << 24) ||
+      (int64_t)kDxN * (K / 2) >= ((int64_t)1 << 32))
+    return p;
+  p.ok = true;
+  p.ktiles = (int)(K / kDxK);
+  p.mtiles = (int)((M + kDxM - 1) / kDxM);
+  const int64_t tiles = (int64_t)p.ktiles * p.mtiles;
+  const int NT = (int)(N / kDxN);
+  const int64_t cus = device_cu_count();
+  int S = (int)std::min<int64_t>(NT, std::max<int64_t>(1, (cus + tiles - 1) / tiles));
+  p.steps = (NT + S - 1) / S;
+  p.splits = (NT + p.steps - 1) / p.steps;  // every split has at least one step
+  if (tiles * p.splits > 0x7fffffff) {
+    p.ok = false;
+    return p;
+  }
+  p.counter_bytes = p.splits > 1 ? (size_t)((tiles * 4 + 255) / 256 * 256) : 0;
+  p.bytes = p.splits > 1 ? p.counter_bytes + (size_t)tiles * p.splits * 4 * 128 * 64 * sizeof(float) : 0;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
 // gemm_4bit_backward: dX[M, K] = dY[M, N] @ W_hat[N, K] ("Feat/mps gemm 4bit
 // bf16", table "What runs natively now": gemm_4bit_backward, the fused form
 // of grad_output @ dequantize_4bit(B)).
@@ -1395,11 +1724,33 @@ __global__ __launch_bounds__(256 * G, 2 / G) void gemm_4bit_dx_kernel(const uint
 template <int ADT>
 static hipError_t launch_backward_t(const void *dY, int64_t M, int64_t N, int64_t K,
                                     const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
-                                    int qt, void *dX, int dx_dtype, hipStream_t st) {
+                                    int qt, void *dX, int dx_dtype, void *ws, hipStream_t st) {
   const uint16_t *g = static_cast<const uint16_t *>(dY);
   Table16f table;
   const uint32_t *bits = table_bits(qt);
   for (int c = 0; c < 16; ++c) table.v[c] = __builtin_bit_cast(float, bits[c]);
+  const DxtPlan p = dxt_plan(M, N, K, log2bs);
+  if (p.ok) {  // the transposed-read kernel (the caller supplied p.bytes of workspace)
+    uint32_t *counters = static_cast<uint32_t *>(ws);
+    float *part = p.splits > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + p.counter_bytes) : nullptr;
+    const dim3 grid((unsigned)((int64_t)p.ktiles * p.mtiles * p.splits));
+    if (p.splits > 1) {
+      hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, st, counters, p.ktiles * p.mtiles);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+#define QMV_T(CDT, DQV)                                                                              \
+  hipLaunchKernelGGL((gemm_4bit_dxt_kernel<ADT, CDT, DQV>), grid, dim3(256), 0, st, g, M, N, K, packed, sc, \
+                     log2bs, table, dX, p.ktiles, p.splits, p.steps, part, counters)
+#define QMV_TD(CDT) \
+  if (dq) { QMV_T(CDT, true); } else { QMV_T(CDT, false); }
+    if (dx_dtype == kF32) { QMV_TD(kF32); }
+    else if (dx_dtype == kF16) { QMV_TD(kF16); }
+    else { QMV_TD(kBF16); }
+#undef QMV_TD
+#undef QMV_T
+    return hipGetLastError();
+  }
   const int64_t mt = (M + 127) / 128;
   const bool wide = ((K + 127) / 128) * mt >= (int64_t)device_cu_count();
   const dim3 grid((unsigned)(wide ? (K + 127) / 128 : (K + 63) / 64), (unsigned)mt);
@@ -1419,11 +1770,16 @@ static hipError_t launch_backward_t(const void *dY, int64_t M, int64_t N, int64_
   return hipGetLastError();
 }
 
+size_t gemm_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int log2bs) {
+  const DxtPlan p = dxt_plan(M, N, K, log2bs);
+  return p.ok ? p.bytes : 0;
+}
+
 hipError_t launch_gemm_4bit_backward(const void *dY, int dy_dtype, int64_t M, int64_t N, int64_t K,
                                      const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
-                                     int qt, void *dX, int dx_dtype, hipStream_t st) {
-  if (dy_dtype == kF16) return launch_backward_t<kF16>(dY, M, N, K, packed, sc, dq, log2bs, qt, dX, dx_dtype, st);
-  return launch_backward_t<kBF16>(dY, M, N, K, packed, sc, dq, log2bs, qt, dX, dx_dtype, st);
+                                     int qt, void *dX, int dx_dtype, void *ws, hipStream_t st) {
+  if (dy_dtype == kF16) return launch_backward_t<kF16>(dY, M, N, K, packed, sc, dq, log2bs, qt, dX, dx_dtype, ws, st);
+  return launch_backward_t<kBF16>(dY, M, N, K, packed, sc, dq, log2bs, qt, dX, dx_dtype, ws, st);
 }
 
 }  // namespace qmv

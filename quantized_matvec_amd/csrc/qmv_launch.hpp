@@ -92,8 +92,10 @@ hipError_t launch_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64
                                  const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
                                  int qt, void *out, int out_dtype, hipStream_t st);
 
+// Bytes of workspace launch_gemm_4bit_backward needs (0: none).
+size_t gemm_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int log2bs);
 hipError_t launch_gemm_4bit_backward(const void *dY, int dy_dtype, int64_t M, int64_t N, int64_t K,
                                      const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
-                                     int qt, void *dX, int dx_dtype, hipStream_t st);
+                                     int qt, void *dX, int dx_dtype, void *ws, hipStream_t st);
 
 }  // namespace qmv

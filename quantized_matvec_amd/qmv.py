@@ -73,7 +73,8 @@ def lib() -> ctypes.CDLL:
         "qmv_quantize_blockwise": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp, vp]),
         "qmv_dequantize_blockwise": (ctypes.c_int, [vp, vp, i64, i32, vp, vp, ctypes.c_int, vp]),
         "qmv_gemm_4bit_backward": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, vp, ap, i32,
-                                                  ctypes.c_int, vp, ctypes.c_int, vp]),
+                                                  ctypes.c_int, vp, ctypes.c_int, vp, sz, vp]),
+        "qmv_gemm_4bit_backward_workspace": (sz, [i64, i64, i64, i32]),
         "qmv_embedding_4bit": (ctypes.c_int, [vp, i64, i64, i64, vp, ap, i32, ctypes.c_int, vp,
                                               ctypes.c_int, vp]),
         "qmv_stream_read": (ctypes.c_int, [vp, i64, vp, vp]),
@@ -336,6 +337,22 @@ def dynamic_tree_code() -> list:
     return list(buf)
 
 
+_BWD_WS: dict = {}
+
+
+def _backward_workspace(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
+    """The backward's workspace for the current stream of ``device`` (calls in
+    order on one stream can share it; a larger request replaces it)."""
+    if nbytes == 0:
+        return None
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _BWD_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _BWD_WS[key] = ws
+    return ws
+
+
 def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState,
                        out: Optional[torch.Tensor] = None,
                        out_dtype: Optional[torch.dtype] = None):
@@ -354,10 +371,13 @@ def gemm_4bit_backward(dY: torch.Tensor, packed: torch.Tensor, state: QuantState
         out = torch.empty((M, K), dtype=out_dtype or dY.dtype, device=dY.device)
     elif not out.is_contiguous() or out.numel() != M * K or out.data_ptr() % 16:
         raise ValueError("out must be contiguous, 16-byte aligned and hold M * K elements")
+    ws = _backward_workspace(lib().qmv_gemm_4bit_backward_workspace(M, N, K, state.blocksize), dY.device)
     c = state._c()
     _check(lib().qmv_gemm_4bit_backward(g2.data_ptr(), _DT[g2.dtype], M, N, K, packed.data_ptr(),
                                         ctypes.byref(c), state.blocksize, _QT[state.quant_type],
-                                        out.data_ptr(), _DT[out.dtype], _stream(g2)),
+                                        out.data_ptr(), _DT[out.dtype],
+                                        ws.data_ptr() if ws is not None else None,
+                                        ws.numel() if ws is not None else 0, _stream(g2)),
            "gemm_4bit_backward")
     return out
 

@@ -34,7 +34,8 @@ def header_functions():
 
 def test_exports_every_declared_symbol(qmvlib):
     names = header_functions()
-    assert len(names) == 18 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
+    assert len(names) == 19 and "qmv_stream_read" in names and "qmv_dynamic_code2" in names
+    assert "qmv_gemm_4bit_backward_workspace" in names
     assert "qmv_double_quant_noalloc" in names
     for n in names:
         assert hasattr(qmvlib, n), n
@@ -148,12 +149,21 @@ def test_matmul_preconditions(qmvlib):
     assert gm(P, 7, 8, 64, 64, P, r, 64, NF4, P, BF16, None, None) == INVALID
     assert gm(P, F16, 8, 64, 64, P, r, 64, NF4, P, F16, P + 1, None) == ALIGN
     gb = qmvlib.qmv_gemm_4bit_backward  # dY [M, N] @ W_hat [N, K]
-    assert gb(P, F32, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED    # dY 16-bit only
-    assert gb(P, BF16, 8, 48, 64, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # N % 32
-    assert gb(P, BF16, 8, 64, 96, P, r, 64, NF4, P, BF16, None) == UNSUPPORTED   # K % bs
-    assert gb(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
-    assert gb(None, BF16, 8, 64, 64, P, r, 64, NF4, P, BF16, None) == INVALID
-    assert gb(P, BF16, 8, 64, 64, P, r, 64, NF4, MIS, BF16, None) == ALIGN
+    assert gb(P, F32, 8, 64, 64, P, r, 64, NF4, P, BF16, None, 0, None) == UNSUPPORTED    # dY 16-bit only
+    assert gb(P, BF16, 8, 48, 64, P, r, 64, NF4, P, BF16, None, 0, None) == UNSUPPORTED   # N % 32
+    assert gb(P, BF16, 8, 64, 96, P, r, 64, NF4, P, BF16, None, 0, None) == UNSUPPORTED   # K % bs
+    assert gb(P, BF16, 0, 64, 64, P, r, 64, NF4, P, BF16, None, 0, None) == INVALID
+    assert gb(None, BF16, 8, 64, 64, P, r, 64, NF4, P, BF16, None, 0, None) == INVALID
+    assert gb(P, BF16, 8, 64, 64, P, r, 64, NF4, MIS, BF16, None, 0, None) == ALIGN
+    # the split reduction's workspace: sized by its query, checked before any launch
+    need = qmvlib.qmv_gemm_4bit_backward_workspace(512, 14336, 4096, 64)
+    assert need > 0 and need % 256 == 0
+    assert qmvlib.qmv_gemm_4bit_backward_workspace(512, 14336, 4096, 32) == 0   # blocks < 64: no split
+    assert qmvlib.qmv_gemm_4bit_backward_workspace(512, 14336, 4000, 32) == 0   # K % 256
+    WS = 0x100000
+    assert gb(P, BF16, 512, 14336, 4096, P, r, 64, NF4, P, BF16, None, 0, None) == WORKSPACE
+    assert gb(P, BF16, 512, 14336, 4096, P, r, 64, NF4, P, BF16, WS, need - 1, None) == WORKSPACE
+    assert gb(P, BF16, 512, 14336, 4096, P, r, 64, NF4, P, BF16, WS + 8, need, None) == WORKSPACE
 
 
 def test_binding_refuses_cpu_tensors(qmvlib):

@@ -49,6 +49,51 @@ def test_backward_shapes(M, N, K, bs, qt, dq):
         check_backward(f64(dX), f64(dY), Wh, "bf16", od, f"{(M, N, K, od)}")
 
 
+@pytest.mark.parametrize("M,N,K,bs", [(130, 320, 256, 128), (256, 640, 512, 64), (1000, 1024, 1024, 64),
+                                      (2048, 384, 2048, 256), (2048, 256, 4096, 64)])
+@pytest.mark.parametrize("dq", [False, True])
+def test_backward_split_reduction(M, N, K, bs, dq):
+    """Shapes the transposed-read kernel takes (N % 64 == 0, K % 256 == 0,
+    blocks of 64 or more): its reduction split over 5, 10, 8, 2 and 1
+    workgroups per 128 x 256 tile (one to three steps of 64 rows each, and
+    ragged row tiles at M = 130 and 1000).  Compared with the oracle, and
+    repeated: the splits are added in a fixed order, so a second call gives
+    the same bits.  The shapes run in one workspace, so a call's tile
+    counters sit where an earlier shape left partial sums."""
+    W = synth.gaussian((N, K), 0.02, 5 * N + K, "bf16")
+    dY = synth.gaussian((M, N), 1.0, 11 * M + N, "bf16")
+    p_ref, ahat = oracle_state(f64(W), bs, "nf4", dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "nf4", double_quant=dq)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    Wh = O.dequantize_4bit(p_ref, ahat, N * K, bs, "nf4").reshape(N, K)
+    print(f"[backward] split path {(M, N, K, bs, dq)}", flush=True)
+    for od in (torch.bfloat16, torch.float32):
+        d1 = qmv.gemm_4bit_backward(dY.cuda(), packed, st, out_dtype=od)
+        d2 = qmv.gemm_4bit_backward(dY.cuda(), packed, st, out_dtype=od)
+        assert torch.equal(d1.view(torch.int16) if od != torch.float32 else d1.view(torch.int32),
+                           d2.view(torch.int16) if od != torch.float32 else d2.view(torch.int32))
+        check_backward(f64(d1), f64(dY), Wh, "bf16", od, f"{(M, N, K, od)}")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_backward_split_identity_rows_exact(dt):
+    """The transposed-read kernel with dY = rows of the identity returns the
+    weight rows as dequantize_4bit gives them in dY's type, bit for bit: the
+    transposition moves every decoded value to the right place, and the
+    split reduction adds only exact zeros to it."""
+    N, K, bs = 256, 512, 64
+    W = synth.gaussian((N, K), 0.02, 23, "bf16")
+    packed, st = qmv.quantize_4bit(W.cuda(), bs, "fp4", double_quant=True)
+    want = qmv.dequantize_4bit(packed, st, out_dtype=dt).cpu().view(torch.int16).numpy().view(np.uint16)
+    dY = torch.eye(N, dtype=dt)[3:3 + 200]
+    got = qmv.gemm_4bit_backward(dY.cuda(), packed, st).cpu().view(torch.int16).numpy().view(np.uint16).copy()
+    want = want[3:3 + 200].copy()
+    sign0 = 0x8000
+    want[want == sign0] = 0
+    got[got == sign0] = 0
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("qt", ["nf4", "fp4"])
 def test_backward_identity_rows_exact(qt):
     """dY = rows of the identity: dX row i is weight row i, dequantized to
