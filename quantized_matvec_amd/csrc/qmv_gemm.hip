@@ -1178,19 +1178,20 @@ hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, in
 // dX[M, K] = dY[M, N] @ W_hat[N, K] with the reduction over N, whose packed
 // rows run along K: the weight tile has to be turned around before the
 // matrix cores can take it as their B operand (8 consecutive reduction
-// values n per lane).  A workgroup of 4 waves owns a 128 (M) x 256 (K) tile
-// of dX and a contiguous range of reduction steps of 64 rows of W; wave w
-// computes all 128 rows x columns [64 w, 64 w + 64) as 4 x 2 accumulators of
-// v_mfma_f32_32x32x16_bf16 (f16).  Per step:
+// values n per lane).  A workgroup of 8 waves owns a 128 (M) x 256 (K) tile
+// of dX and a contiguous range of reduction steps of 64 rows of W; wave
+// (h, g) computes rows [64 h, 64 h + 64) x columns [64 g, 64 g + 64) as 2 x 2
+// accumulators of v_mfma_f32_32x32x16_bf16 (f16), two waves per SIMD.  Per
+// step:
 //  * dY's 128 x 64 tile goes global -> LDS through 16-byte LDS-direct loads
 //    into a 3-stage ring issued two steps ahead (the forward large-M
 //    kernel's activation ring, with n in place of k);
-//  * lane l of wave w decodes row n0 + l of the step, columns [64 w, + 64):
-//    two 16-byte packed loads, one block scale (blocks >= 64 columns), 32
-//    lookups of the fp32 pair table, fp32(T * a_hat) rounded to dY's type
-//    -- exactly the dequantize_4bit values -- and writes the 128-byte row
-//    into the wave's own 64 x 64 LDS block (no other wave reads it, so no
-//    barrier guards it);
+//  * the two waves of column group g decode its 64 rows of the step, columns
+//    [64 g, + 64): lane l of wave (h, g) takes row 32 h + l / 2, 32 columns
+//    (one 16-byte packed load, one block scale: blocks >= 64 columns), 16
+//    lookups of the fp32 pair table, fp32(T * a_hat) rounded to dY's type --
+//    exactly the dequantize_4bit values -- and writes its 64 bytes into the
+//    group's 64 x 64 LDS block; a barrier then makes the block whole;
 //  * the B operand comes back out of that block with ds_read_b64_tr_b16:
 //    within each 16 lanes the instruction returns, to lane i, element i % 4
 //    of what lanes 4 e + i / 4 (e = 0..3) addressed, so lanes that address 4
@@ -1208,9 +1209,9 @@ hipError_t launch_gemm_4bit(const void *A, int a_dtype, int64_t M, int64_t N, in
 // first (a workspace that served another shape may hold partials where the
 // counters are now).  The workgroups of a
 // tile run on different XCDs, whose L2 caches are not coherent with each
-// other for ordinary accesses: the partials and the counter are written and
-// read with agent-scope atomic accesses, which bypass the non-coherent
-// caches.
+// other for ordinary accesses: the partials are written and read with the
+// SC1 cache policy and the counter with an agent-scope atomic, which bypass
+// the non-coherent caches.
 // ---------------------------------------------------------------------------
 constexpr int kDxM = 128, kDxK = 256, kDxN = 64;
 
@@ -1220,7 +1221,7 @@ __device__ __forceinline__ int dxt_swz(int n) {  // 16-byte chunk swizzle of wei
 }
 
 template <int ADT, int CDT, bool DQ>
-__global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
+__global__ __launch_bounds__(512, 1) void gemm_4bit_dxt_kernel(
     const uint16_t *__restrict__ dY, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ packed,
     Scales sc, int log2bs, Table16f table, void *__restrict__ dXv, int ktiles, int splits, int steps_per_split,
     float *__restrict__ part, uint32_t *__restrict__ counters) {
@@ -1229,10 +1230,12 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 32 * 2];  // byte -> (T[hi], T[lo]), 32 copies
   __shared__ float code2[256];
   __shared__ uint4 st0[kDxM * 8], st1[kDxM * 8], st2[kDxM * 8];       // dY ring
-  __shared__ __attribute__((aligned(16))) uint4 wbuf[4 * kDxN * 8];  // decoded weights, 8 KB per wave
+  __shared__ __attribute__((aligned(16))) uint4 wbuf[4 * kDxN * 8];  // decoded weights, 8 KB per column group
   __shared__ int last_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = wave & 3;   // column group: dX columns [64 cg, 64 cg + 64) of the tile
+  const int mh = wave >> 2;  // row half: dX rows [64 mh, 64 mh + 64) of the tile
   const int s = (int)blockIdx.x % splits;
   const int tile = (int)blockIdx.x / splits;
   const int64_t m0 = (int64_t)(tile / ktiles) * kDxM;
@@ -1244,50 +1247,53 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
     const uint32_t lo = __float_as_uint(table.v[(tid >> 4) & 15]);
     uint4 *dst = reinterpret_cast<uint4 *>(lut);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const uint32_t hi = __float_as_uint(table.v[it]);
-      dst[it * 256 + tid] = make_uint4(hi, lo, hi, lo);
+    for (int it = 0; it < 8; ++it) {  // chunk it * 512 + tid: entry hi nibble 2 it + tid / 256
+      const uint32_t hi = __float_as_uint((tid >> 8) ? table.v[2 * it + 1] : table.v[2 * it]);
+      dst[it * 512 + tid] = make_uint4(hi, lo, hi, lo);
     }
   }
   float offset = 0.f;
   if constexpr (DQ) {
-    code2[tid] = sc.code2[tid];
+    if (tid < 256) code2[tid] = sc.code2[tid];
     offset = sc.offset[0];
   }
-  // dY: wave w moves rows (4 w + d) * 8 + l / 8 of a stage, lane l into
+  // dY: wave w moves rows (2 w + d) * 8 + l / 8 of a stage, lane l into
   // position l % 8 of its row, from chunk (l % 8) ^ ((row / 2) % 8); rows past
   // M read zeros (bounded resource)
   const int64_t mrows = M - m0 < kDxM ? M - m0 : kDxM;
   const uint16_t *a_base = dY + m0 * N;
   const uint32_t a_bytes = (uint32_t)(mrows * N * 2);
-  uint32_t aoff[4];
+  uint32_t aoff[2];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int r = (4 * wave + d) * 8 + (lane >> 3);
+  for (int d = 0; d < 2; ++d) {
+    const int r = (2 * wave + d) * 8 + (lane >> 3);
     aoff[d] = (uint32_t)(r * N * 2) + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
-  auto issue_a = [&](int l, uint4 *stage) {  // step l of this split; steps past the end re-read the last
+  auto issue_a = [&](int l, uint4 *stage) __attribute__((always_inline)) {
+    // step l of this split; steps past the end re-read the last
     const uint32_t no = (uint32_t)(nt0 + (l < nsteps ? l : nsteps - 1)) * (kDxN * 2);
     const __amdgpu_buffer_rsrc_t ars = make_rsrc_u(a_base, a_bytes);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) load_lds16(ars, stage + (4 * wave + d) * 64, aoff[d] + no);
+    for (int d = 0; d < 2; ++d) load_lds16(ars, stage + (2 * wave + d) * 64, aoff[d] + no);
   };
-  // weights: lane l -> row n0 + l of the step, columns k0 + 64 w .. + 63 (32 bytes, one block)
+  // weights: the two waves of a column group decode its 64 rows of the step,
+  // wave (mh, cg) rows 32 mh .. 32 mh + 31: lane l takes row 32 mh + l / 2,
+  // columns k0 + 64 cg + 32 (l % 2) .. + 31 (one 16-byte load, one block)
   const uint32_t rowb = (uint32_t)(K >> 1);
-  const int64_t kcol = k0 + 64 * wave;
+  const int64_t kcol = k0 + 64 * cg;
   const int64_t bpr = K >> log2bs;  // blocks per weight row
+  const int wrow = 32 * mh + (lane >> 1);
   struct BR {
-    uint4 w[2];
+    uint4 w;
     uint32_t q;
     float s;
   };
-  auto issue_b = [&](int l, BR &b) {
+  auto issue_b = [&](int l, BR &b) __attribute__((always_inline)) {
     const int64_t row0 = (int64_t)(nt0 + (l < nsteps ? l : nsteps - 1)) * kDxN;
     const __amdgpu_buffer_rsrc_t prs = make_rsrc_u(packed + row0 * rowb, kDxN * rowb);
-    const uint32_t off = (uint32_t)lane * rowb + (uint32_t)(kcol >> 1);
-    b.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0));
-    b.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, off + 16u, 0, 0));
-    const int64_t blk = (row0 + lane) * bpr + (kcol >> log2bs);
+    const uint32_t off = (uint32_t)wrow * rowb + (uint32_t)(kcol >> 1) + 16u * (uint32_t)(lane & 1);
+    b.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0));
+    const int64_t blk = (row0 + wrow) * bpr + (kcol >> log2bs);
     if constexpr (DQ) {
       b.q = sc.q[blk];
       b.s = sc.absmax2[blk >> sc.log2bs2];
@@ -1302,9 +1308,9 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
   issue_b(1, br1);
   __syncthreads();  // table and code2
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1312,16 +1318,15 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
 
   const uint32_t lane_sel = (uint32_t)(lane & 31) << 3;
   const char *lut_b = reinterpret_cast<const char *>(lut);
-  uint4 *wmine = wbuf + wave * (kDxN * 8);
-  const int wsw = dxt_swz(lane);  // this lane's row is row `lane` of the block
-  // decode row `lane` of the step into the wave's block, chunk p (8 values,
-  // columns 8 p .. 8 p + 7) at position p ^ swizzle
+  uint4 *wblk = wbuf + cg * (kDxN * 8);  // the column group's decoded 64 x 64 block
+  const int wsw = dxt_swz(wrow);
+  // decode this lane's 32 columns of row wrow: chunk p (columns 8 p .. 8 p + 7
+  // of the block) at position p ^ swizzle
   auto decode = [&](const BR &b) __attribute__((always_inline)) {
     const float a = DQ ? code2[b.q & 255u] * b.s + offset : b.s;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const uint32_t w = (p >> 2) == 0 ? ((p & 3) == 0 ? b.w[0].x : (p & 3) == 1 ? b.w[0].y : (p & 3) == 2 ? b.w[0].z : b.w[0].w)
-                                       : ((p & 3) == 0 ? b.w[1].x : (p & 3) == 1 ? b.w[1].y : (p & 3) == 2 ? b.w[1].z : b.w[1].w);
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint32_t w = pp == 0 ? b.w.x : pp == 1 ? b.w.y : pp == 2 ? b.w.z : b.w.w;
       float2 tv[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
@@ -1331,7 +1336,8 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
       uint32_t o[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) o[bb] = cvt_pair<ADT>(tv[bb].x * a, tv[bb].y * a);
-      wmine[lane * 8 + (p ^ wsw)] = make_uint4(o[0], o[1], o[2], o[3]);
+      const int p = 4 * (lane & 1) + pp;
+      wblk[wrow * 8 + (p ^ wsw)] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
   // transposed B operand of MFMA step t (reduction rows 16 t + 8 h .. + 7)
@@ -1349,7 +1355,7 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
       const int u = 8 * j + 4 * ((lane >> 4) & 1) + (lane & 3);  // 8-byte unit of the row
       const int phys = ((((u >> 1) ^ dxt_swz(n)) << 1) | (u & 1));
       const v4s_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4s_t *)(reinterpret_cast<char *>(wmine) + n * 128 + phys * 8));
+          (lds_v4s_t *)(reinterpret_cast<char *>(wblk) + n * 128 + phys * 8));
       const uint2 xx = __builtin_bit_cast(uint2, x);
       v[2 * r] = xx.x;
       v[2 * r + 1] = xx.y;
@@ -1362,8 +1368,8 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
       const bf16x8_t b0 = bfrag(t, 0), b1 = bfrag(t, 1);
       const int c = 2 * t + h;  // this lane's 16-byte chunk of the dY row for MFMA t
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 32 * i + colw;
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * mh + 32 * i + colw;
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ ((r >> 1) & 7))]);
         acc[i][0] = mfma16<ADT>(af, b0, acc[i][0]);
         acc[i][1] = mfma16<ADT>(af, b1, acc[i][1]);
@@ -1377,14 +1383,15 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
   // their scattered block scales stall the step)
   auto step = [&](int l, uint4 *sa_cur, uint4 *sa_next2, BR &bcur, BR &bnext2) __attribute__((always_inline)) {
     // dY(l) must have landed for every wave: this wave's loads issued since
-    // are W(l) and dY(l + 1), W(l + 1) (4 + 2 x (2 + 2), or 2 + 1 per W
+    // are W(l) and dY(l + 1), W(l + 1) (2 + 2 x (1 + 2), or 1 + 1 per W
     // without double quantization)
-    constexpr int after = 4 + 2 * (DQ ? 4 : 3);
+    constexpr int after = 2 + 2 * (DQ ? 3 : 2);
     __builtin_amdgcn_s_waitcnt((after & 15) | (7 << 4) | (15 << 8) | ((after >> 4) << 14));
-    __syncthreads();  // and every wave is done with stage (l + 2) % 3
+    __syncthreads();  // and every wave is done with stage (l + 2) % 3 and with the weight blocks
     issue_a(l + 2, sa_next2);
     issue_b(l + 2, bnext2);
     decode(bcur);
+    __syncthreads();  // both halves of every column group's block are written
     mma(sa_cur);
   };
   int l = 0;
@@ -1401,64 +1408,72 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_dxt_kernel(
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no LDS-direct load outlives the loop
 
   if (splits > 1) {
-    // this split's partial tile, lane-major per wave: element e of lane l at
-    // e * 64 + l
-    float *mine = part + ((int64_t)(tile * splits + s) * 4 + wave) * (128 * 64);
+    // this split's partial tile, per wave 16-byte pieces: elements 4 c ..
+    // 4 c + 3 of lane l at piece c * 64 + l.  Stored and later read with the
+    // SC1 cache policy (coherent at agent scope: the non-coherent caches are
+    // bypassed), 16 bytes per lane per instruction.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int kSC1 = 16;  // cache-policy bit SC1
+    constexpr int kPer = 64 * 64;  // floats per wave
+    float *mine = part + ((int64_t)(tile * splits + s) * 8 + wave) * kPer;
+    {
+      const __amdgpu_buffer_rsrc_t mrs = make_rsrc(mine, kPer * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)  // agent-scope stores: coherent across the XCDs' L2 caches
-          __hip_atomic_store(mine + ((i * 2 + j) * 16 + r) * 64 + lane, acc[i][j][r], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    // the partial's agent-scope stores write through to the point of
-    // coherence; waiting for their completion (vmcnt(0)) in every wave
-    // before the count is bumped publishes them.  No release or acquire
-    // fence: at agent scope those write back and invalidate the whole L2 of
-    // the XCD (measured: +33 us on 512 x 14336 x 4096), and nothing else
-    // this kernel writes needs publishing.
+      for (int c = 0; c < 16; ++c) {
+        const int i = c >> 3, j = (c >> 2) & 1, r0 = 4 * (c & 3);
+        const u32x4_t v = {__float_as_uint(acc[i][j][r0]), __float_as_uint(acc[i][j][r0 + 1]),
+                           __float_as_uint(acc[i][j][r0 + 2]), __float_as_uint(acc[i][j][r0 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, mrs, (uint32_t)((c * 64 + lane) * 16), 0, kSC1);
+      }
+    }
+    // the partial's SC1 stores write through to the point of coherence;
+    // waiting for their completion (vmcnt(0)) in every wave before the count
+    // is bumped publishes them.  No release or acquire fence: at agent scope
+    // those write back and invalidate the whole L2 of the XCD (measured: +33
+    // us on 512 x 14336 x 4096), and nothing else this kernel writes needs
+    // publishing.
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
     __syncthreads();
     if (tid == 0)
       last_flag = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                   (uint32_t)(splits - 1);
     __syncthreads();
-    if (!last_flag) return;  // the partials are read below with agent-scope (coherent) loads
-    // the S partials added in split order, 64 elements at a time with all
-    // of a split's loads in flight together
-    const float *base = part + (int64_t)tile * splits * 4 * (128 * 64) + wave * (128 * 64) + lane;
+    if (!last_flag) return;  // the partials are read below with SC1 (coherent) loads
+    // the S partials added in split order, all of a split's loads in flight
+    // together
+    float sum[64];
+    for (int s2 = 0; s2 < splits; ++s2) {
+      float v[64];
+      if (s2 == s) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float sum[64];
-      for (int s2 = 0; s2 < splits; ++s2) {
-        float v[64];
-        if (s2 == s) {
+        for (int e = 0; e < 64; ++e) v[e] = acc[e >> 5][(e >> 4) & 1][e & 15];
+      } else {
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc(part + ((int64_t)(tile * splits + s2) * 8 + wave) * kPer, kPer * 4);
 #pragma unroll
-          for (int e = 0; e < 64; ++e) v[e] = acc[(64 * half + e) >> 5][((64 * half + e) >> 4) & 1][e & 15];
-        } else {
-          const float *src = base + (int64_t)s2 * 4 * (128 * 64) + (64 * half) * 64;
-#pragma unroll
-          for (int e = 0; e < 64; ++e)
-            v[e] = __hip_atomic_load(src + e * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < 16; ++c) {
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(prs, (uint32_t)((c * 64 + lane) * 16), 0, kSC1);
+          v[4 * c] = __uint_as_float(x.x);
+          v[4 * c + 1] = __uint_as_float(x.y);
+          v[4 * c + 2] = __uint_as_float(x.z);
+          v[4 * c + 3] = __uint_as_float(x.w);
         }
-#pragma unroll
-        for (int e = 0; e < 64; ++e) sum[e] = s2 == 0 ? v[e] : sum[e] + v[e];
       }
 #pragma unroll
-      for (int e = 0; e < 64; ++e) acc[(64 * half + e) >> 5][((64 * half + e) >> 4) & 1][e & 15] = sum[e];
+      for (int e = 0; e < 64; ++e) sum[e] = s2 == 0 ? v[e] : sum[e] + v[e];
     }
+#pragma unroll
+    for (int e = 0; e < 64; ++e) acc[e >> 5][(e >> 4) & 1][e & 15] = sum[e];
   }
 
   // 32 x 32 accumulator layout: column = lane % 32, row = 8 (r / 4) + 4 (lane / 32) + r % 4
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = kcol + 32 * j + colw;  // < K: K % 256 == 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t row = m0 + 64 * mh + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < M) store_elem<CDT>(dX, row * K + col, acc[i][j][r]);
       }
     }
@@ -1740,7 +1755,7 @@ static hipError_t launch_backward_t(const void *dY, int64_t M, int64_t N, int64_
       if (e != hipSuccess) return e;
     }
 #define QMV_T(CDT, DQV)                                                                              \
-  hipLaunchKernelGGL((gemm_4bit_dxt_kernel<ADT, CDT, DQV>), grid, dim3(256), 0, st, g, M, N, K, packed, sc, \
+  hipLaunchKernelGGL((gemm_4bit_dxt_kernel<ADT, CDT, DQV>), grid, dim3(512), 0, st, g, M, N, K, packed, sc, \
                      log2bs, table, dX, p.ktiles, p.splits, p.steps, part, counters)
 #define QMV_TD(CDT) \
   if (dq) { QMV_T(CDT, true); } else { QMV_T(CDT, false); }
