@@ -794,7 +794,8 @@ __global__ __launch_bounds__(256, 2) void gemm_4bit_f32_kernel(const float *__re
 //    copies, one per lane of a half-wave (no bank conflicts); the weights
 //    are fp32(T * a_hat) rounded to the input type, exactly the
 //    dequantize_4bit values;
-//  * the next k-tile's packed weights and scales are loaded meanwhile.
+//  * the packed weights and scales are loaded two k-tiles ahead, into three
+//    register sets.
 // Workgroups are ordered so that the row tiles of one column tile run on one
 // XCD (dispatch is round-robin over the 8 XCDs): its packed weights are read
 // from HBM once and then from that XCD's L2.
@@ -914,8 +915,9 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
   };
   issue_a(0, st0);
   issue_a(1, st1);
-  BR br0, br1;
+  BR br0, br1, br2;
   issue_b(0, br0);
+  issue_b(1, br1);
   __syncthreads();  // table and code2
 
   f32x16_t acc[4][2];
@@ -965,35 +967,33 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<ADT>(af[i], bf[j][t], acc[i][j]);
     }
   };
-  // iteration kt: A(kt) in stage kt % 3, B(kt) in register set kt % 2
-  auto step = [&](int kt, uint4 *sa_cur, uint4 *sa_next2, BR &bcur, BR &bnext) {
+  // iteration kt: A(kt) in stage kt % 3, B(kt) in register set kt % 3, both
+  // loaded two k-tiles ahead (loads complete in order, so the wait for a
+  // k-tile's weights also waits for everything issued before them: with two
+  // k-tiles between issue and use neither stream stalls the step)
+  auto step = [&](int kt, uint4 *sa_cur, uint4 *sa_next2, BR &bcur, BR &bnext2) {
     // A(kt) must have landed for every wave: this wave's loads issued since
-    // are A(kt + 1) (4) and B(kt) (2 + 4, or 2 + 2 without double quantization)
-    constexpr int after = 4 + (DQ ? 6 : 4);
+    // are B(kt), A(kt + 1) and B(kt + 1) (4 + 2 x (2 + 4), or 2 + 2 per B
+    // without double quantization)
+    constexpr int after = 4 + 2 * (DQ ? 6 : 4);
     __builtin_amdgcn_s_waitcnt((after & 15) | (7 << 4) | (15 << 8) | ((after >> 4) << 14));
     __syncthreads();  // and every wave is done with stage (kt + 2) % 3
     issue_a(kt + 2, sa_next2);
-    issue_b(kt + 1, bnext);
+    issue_b(kt + 2, bnext2);
     bf16x8_t bf[2][4];
     decode(bcur, bf);
     mma(sa_cur, bf);
   };
   int kt = 0;
-  for (; kt + 6 <= KT; kt += 6) {
-    step(kt, st0, st2, br0, br1);
+  for (; kt + 3 <= KT; kt += 3) {
+    step(kt, st0, st2, br0, br2);
     step(kt + 1, st1, st0, br1, br0);
-    step(kt + 2, st2, st1, br0, br1);
-    step(kt + 3, st0, st2, br1, br0);
-    step(kt + 4, st1, st0, br0, br1);
-    step(kt + 5, st2, st1, br1, br0);
+    step(kt + 2, st2, st1, br2, br1);
   }
-  {  // the remaining 0..5 k-tiles (kt is a multiple of 6 here)
+  {  // the remaining 0..2 k-tiles (kt is a multiple of 3 here)
     const int rem = KT - kt;
-    if (rem > 0) step(kt, st0, st2, br0, br1);
+    if (rem > 0) step(kt, st0, st2, br0, br2);
     if (rem > 1) step(kt + 1, st1, st0, br1, br0);
-    if (rem > 2) step(kt + 2, st2, st1, br0, br1);
-    if (rem > 3) step(kt + 3, st0, st2, br1, br0);
-    if (rem > 4) step(kt + 4, st1, st0, br0, br1);
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no LDS-direct load outlives the kernel
 
