@@ -1078,9 +1078,20 @@ static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
 #define QMV_N(CDT, DQV, MPV, NBV, KWV)                                                          \
   hipLaunchKernelGGL((gemm_4bit_narrow_kernel<ADT, CDT, DQV, MPV, NBV, KWV>), sgrid, dim3(64 * KWV), \
                      0, st, a, M, N, K, packed, sc, log2bs, table, C, bias)
-#define QMV_NM(CDT, DQV)                        \
-  if (M <= 8) { QMV_N(CDT, DQV, 8, 2, 4); }     \
-  else { QMV_N(CDT, DQV, 16, 2, 4); }
+    // waves per workgroup splitting K: more when the N / 32 workgroups leave
+    // compute units with few waves (8192 columns: one workgroup per CU), as
+    // long as every wave still gets a few 128-k groups
+    const int64_t cus = device_cu_count(), groups = (K / 64 + 1) / 2;
+    const int kw = (g.gx <= cus && groups >= 32) ? 16 : ((g.gx <= 2 * cus && groups >= 16) ? 8 : 4);
+#define QMV_NM(CDT, DQV)                                                        \
+  if (M <= 8) {                                                                 \
+    if (kw == 16) { QMV_N(CDT, DQV, 8, 2, 16); }                                \
+    else if (kw == 8) { QMV_N(CDT, DQV, 8, 2, 8); }                             \
+    else { QMV_N(CDT, DQV, 8, 2, 4); }                                          \
+  } else {                                                                      \
+    if (kw >= 8) { QMV_N(CDT, DQV, 16, 2, 8); }                                 \
+    else { QMV_N(CDT, DQV, 16, 2, 4); }                                         \
+  }
 #define QMV_ND(CDT) \
   if (dq) { QMV_NM(CDT, true); } else { QMV_NM(CDT, false); }
     if (c_dtype == kF32) { QMV_ND(kF32); }

@@ -210,6 +210,30 @@ def test_gemm_narrow_identity_rows_exact(qt, rows):
     assert np.array_equal(Cb, O.f32_to_bf16_bits(want))
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 1000, 4096), (3, 8200, 4160), (12, 2000, 2048), (16, 640, 8192),
+                                   (8, 256, 1024)])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemm_narrow_many_waves(M, N, K, dq):
+    """When N / 32 workgroups leave compute units with few waves the narrow
+    kernel splits K over 8 or 16 waves per workgroup: 16 waves (32 or 20
+    column groups with 32 or 64 groups of 128 k-values), 8 waves (257
+    workgroups, K = 4160 ending on half a group; 16 rows with 16 groups),
+    and 4 waves where K is too short to share (8 column groups, 16 k-groups
+    but 16 waves would get one each)."""
+    W = gaussian((N, K), 0.02, 3 * M + N + dq, "bf16")
+    A = gaussian((M, K), 1.0, M + K + 1, "bf16")
+    p_ref, ahat = oracle_state(f64(W), 64, "nf4", dq)
+    packed, st = qmv.quantize_4bit(W.cuda(), 64, "nf4", double_quant=dq)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    Wh = w_hat(p_ref, ahat, N, K, 64, "nf4")
+    for od in (torch.bfloat16, torch.float32):
+        C = qmv.gemm_4bit(A.cuda(), packed, st, out_dtype=od)
+        check_matmul(f64(C), f64(A), Wh, "bf16", od, f"M={M} N={N} K={K} dq={dq} {od}")
+        if M <= 8:  # the gemv entry point takes the same kernel for 4 to 8 rows
+            y = qmv.gemv_4bit(A.cuda(), packed, st, out_dtype=od)
+            check_matmul(f64(y), f64(A), Wh, "bf16", od, f"gemv M={M} N={N} K={K} dq={dq} {od}")
+
+
 @pytest.mark.parametrize("M", [1, 2, 8, 9, 16, 17, 31, 32, 33, 64, 65])
 @pytest.mark.parametrize("K", [96, 192, 1600])
 @pytest.mark.parametrize("dq", [False, True])
