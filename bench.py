@@ -26,7 +26,10 @@ double-quantized scales) with gemv_4bit at M = 1, 2, 4, 8.  Each row gives
 microseconds per launch, algorithmic bytes (and flops for gemm), the fraction
 of the HBM peak and of the measured read (gemv) or copy (codec) ceiling.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-configs]
+Before anything is timed, untimed steps run for --warm-seconds (2 s) so that
+the GPU clocks have ramped up.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--warm-seconds S] [--no-cpu-baseline] [--no-configs]
 """
 from __future__ import annotations
 
@@ -435,6 +438,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=2.0,
+                    help="untimed steps for this long first, so the GPU clocks have ramped up")
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
@@ -503,6 +508,16 @@ def main():
                                                  Ws[i % n_w], BS, "nf4")), n_p, dev, torch)
             return
 
+        # the clocks ramp up under load over the first second or so (the same
+        # kernel measured 15 % slower at the start of a run than after it):
+        # run untimed steps for --warm-seconds, then the W warm-up steps
+        tw = time.perf_counter()
+        i = 0
+        while time.perf_counter() - tw < args.warm_seconds:
+            step(i)
+            i += 1
+            if i % 20 == 0:
+                torch.cuda.synchronize()
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
