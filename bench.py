@@ -440,7 +440,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=2.0,
                     help="untimed steps for this long first, so the GPU clocks have ramped up")
-    ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload table (every weight, quant type and row count)")
@@ -526,8 +525,7 @@ def main():
         torch.cuda.synchronize()
         wall_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-        kiters = args.kernel_iters
-        kern = {}
+        kern, kern_iters = {}, {}
         # per-kernel loops call the C ABI directly with prepared arguments,
         # so the host keeps ahead of kernels of a few microseconds
         L = qmv.lib()
@@ -607,22 +605,19 @@ def main():
             return L.qmv_embedding_4bit(eidx.data_ptr(), EMB_T, EMB_V, K, pe.data_ptr(), ctypes.byref(ec), BS, 0,
                                         eout.data_ptr(), 2, s_h)
 
-        for name, fn, iters in (("gemv_4bit", run_gemv, kiters), ("gemm_4bit", run_gemm, kiters // 4),
-                                ("gemm_4bit_backward", run_bwd, kiters // 8),
-                                ("dequantize_4bit", run_deq, kiters // 4),
-                                ("quantize_4bit", run_quant, kiters // 4),
-                                ("double_quant", run_dq, kiters // 4),
-                                ("quantize_blockwise", run_q8, kiters // 4),
-                                ("quantize_blockwise_dynamic", lambda i: run_q8(i, tree_p), kiters // 4),
-                                ("dequantize_blockwise", run_dq8, kiters // 4),
-                                ("embedding_4bit", run_emb, kiters // 4)):
-            for i in range(5):
-                _ok(fn(i))
-            kern[name] = timed_loop(fn, iters, stream, torch)
+        # each loop runs about 30 ms of launches (a short loop right after a
+        # memory-bound one reads a compute-bound kernel up to 15 % slow)
+        for name, fn in (("gemv_4bit", run_gemv), ("gemm_4bit", run_gemm), ("gemm_4bit_backward", run_bwd),
+                         ("dequantize_4bit", run_deq), ("quantize_4bit", run_quant), ("double_quant", run_dq),
+                         ("quantize_blockwise", run_q8), ("quantize_blockwise_dynamic", lambda i: run_q8(i, tree_p)),
+                         ("dequantize_blockwise", run_dq8), ("embedding_4bit", run_emb)):
+            us, it = _auto_timed(fn, stream, torch, hi=4000)
+            kern[name] = us
+            kern_iters[name] = it
 
     rep = {}
     for name, us in kern.items():
-        e = {"us_per_launch": round(us, 3)}
+        e = {"us_per_launch": round(us, 3), "launches_timed": kern_iters[name]}
         if name in ("gemm_4bit", "gemm_4bit_backward"):
             fl = 2.0 * M_GEMM * N * K
             e.update(flops=fl, tflops=round(fl / us / 1e6, 2),
