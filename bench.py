@@ -657,7 +657,10 @@ def main():
                      "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "gemv_4bit",
                      "algorithmic_bytes_per_launch": ab["gemv_4bit"], "avg_launch_us": round(gemv_us, 3),
-                     "frac_of_measured_read": round(gemv_gbs / ceil["read_gbs"], 4)},
+                     "frac_of_measured_read": round(gemv_gbs / ceil["read_gbs"], 4),
+                     "note": "avg_launch_us is the interval between back-to-back launches (HIP events around "
+                             "the whole loop); a rocprofv3 kernel trace reports the kernel's own duration, "
+                             "shorter by the dispatch gap between consecutive kernels"},
         "ceilings": ceil,
         "env": {"torch": torch.__version__, "hip": torch.version.hip,
                 "device": torch.cuda.get_device_name(dev),
