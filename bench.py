@@ -122,11 +122,11 @@ def timed_loop(fn, iters, stream, torch):
 def cpu_baseline(W_cpu, x_cpu, A_cpu, budget_s=12.0, rows=256):
     """The oracle as it stands, timed on bounded samples of the headline
     workload (W_up 14336 x 4096 bf16, NF4, block 64, double-quantized scales):
-      quantize_4bit of the first 64 weight rows; double_quant of the first
-      65536 block scales; dequantize_4bit (to bf16) of the first `rows` rows;
+      quantize_4bit of the first 2048 weight rows; double_quant of all
+      917504 block scales; dequantize_4bit (to bf16) of the first 4096 rows;
       gemv (scale decode + dequantize + float64 matmul) over the first `rows`
-      output rows, repeated for `budget_s`; gemm of 64 activation rows against
-      the first `rows` output rows.
+      output rows, repeated for `budget_s`; gemm of the 512 activation rows
+      against the first 1024 output rows.
     Elementwise numpy runs on one thread, the float64 matmuls on all BLAS
     threads.  Bytes and flops are counted per unit exactly as for the GPU
     kernels.  The headline value is the gemv's."""
@@ -137,30 +137,34 @@ def cpu_baseline(W_cpu, x_cpu, A_cpu, budget_s=12.0, rows=256):
     import oracle as O
     W64 = W_cpu.to(torch.float64).numpy()
     x64 = x_cpu.to(torch.float64).numpy()
-    A64 = A_cpu[:64].to(torch.float64).numpy()
+    A64 = A_cpu.to(torch.float64).numpy()
     blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     ops = {}
     with threadpool_limits(limits=1):
         absmax = O.block_absmax(W64, BS).astype(np.float32)      # untimed set-up
-        q, a2, off = O.double_quant(absmax, BS2)
+        q, a2, off = O.double_quant(absmax, BS2, forms="threshold")
         t0 = time.perf_counter()
-        O.quantize_4bit(W64[:64], BS, "nf4")
+        O.quantize_4bit(W64[:2048], BS, "nf4", forms="threshold")
         t = time.perf_counter() - t0
-        ops["quantize_4bit"] = {"gbs": round(64 * K * (2 + 0.5 + 4 / BS) / t / 1e9, 5), "s": round(t, 3),
-                                "sample": "64 rows x 4096"}
+        ops["quantize_4bit"] = {"gbs": round(2048 * K * (2 + 0.5 + 4 / BS) / t / 1e9, 5), "s": round(t, 3),
+                                "sample": "2048 rows x 4096 (threshold form of the nearest-code search)"}
         t0 = time.perf_counter()
-        O.double_quant(absmax[:65536], BS2)
+        O.double_quant(absmax, BS2, forms="threshold")
         t = time.perf_counter() - t0
-        ops["double_quant"] = {"gbs": round(65536 * (4 + 1 + 4 / BS2) / t / 1e9, 5), "s": round(t, 3),
-                               "sample": "65536 scales"}
-        packed, _ = O.quantize_4bit(W64[:rows], BS, "nf4")
+        ops["double_quant"] = {"gbs": round(absmax.size * (4 + 1 + 4 / BS2) / t / 1e9, 5), "s": round(t, 3),
+                               "sample": f"{absmax.size} scales (threshold form)"}
+        drows = 4096
+        packed_d, _ = O.quantize_4bit(W64[:drows], BS, "nf4", forms="threshold")
+        nbd = drows * K // BS
+        ahat_d = O.dequant_absmax(q[:nbd], a2[:-(-nbd // BS2)], off, None, BS2)
+        t0 = time.perf_counter()
+        O.dequantize_4bit(packed_d, ahat_d, drows * K, BS, "nf4", "bf16")
+        t = time.perf_counter() - t0
+        ops["dequantize_4bit"] = {"gbs": round(drows * K * (0.5 + 2 + (1 + 4 / BS2) / BS) / t / 1e9, 5),
+                                  "s": round(t, 3), "sample": f"{drows} rows x 4096"}
+        packed, _ = O.quantize_4bit(W64[:rows], BS, "nf4", forms="threshold")
         nbs = rows * K // BS
         ahat = O.dequant_absmax(q[:nbs], a2[:-(-nbs // BS2)], off, None, BS2)
-        t0 = time.perf_counter()
-        O.dequantize_4bit(packed, ahat, rows * K, BS, "nf4", "bf16")
-        t = time.perf_counter() - t0
-        ops["dequantize_4bit"] = {"gbs": round(rows * K * (0.5 + 2 + (1 + 4 / BS2) / BS) / t / 1e9, 5),
-                                  "s": round(t, 3), "sample": f"{rows} rows x 4096"}
     with threadpool_limits(limits=1, user_api="openmp"), threadpool_limits(limits=blas, user_api="blas"):
         passes, t0 = 0, time.perf_counter()
         while True:
@@ -174,11 +178,15 @@ def cpu_baseline(W_cpu, x_cpu, A_cpu, budget_s=12.0, rows=256):
         gbs = passes * rows * per_row / t_gemv / 1e9
         ops["gemv_4bit"] = {"gbs": round(gbs, 5), "s": round(t_gemv, 3),
                             "sample": f"{rows} output rows, {passes} passes"}
+        grows = 1024
+        packed_g, _ = O.quantize_4bit(W64[:grows], BS, "nf4", forms="threshold")
+        nbg = grows * K // BS
+        ahat_g = O.dequant_absmax(q[:nbg], a2[:-(-nbg // BS2)], off, None, BS2)
         t0 = time.perf_counter()
-        O.matmul_4bit(A64, packed, ahat, rows, K, BS, "nf4")
+        O.matmul_4bit(A64, packed_g, ahat_g, grows, K, BS, "nf4")
         t = time.perf_counter() - t0
-        ops["gemm_4bit"] = {"gflops": round(2 * 64 * rows * K / t / 1e9, 4), "s": round(t, 3),
-                            "sample": f"64 x {rows} outputs, K = 4096"}
+        ops["gemm_4bit"] = {"gflops": round(2 * A64.shape[0] * grows * K / t / 1e9, 4), "s": round(t, 3),
+                            "sample": f"{A64.shape[0]} x {grows} outputs, K = 4096"}
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": blas, "kind": "oracle",
             "sample": f"oracle gemv (DQ scale decode + dequantize + float64 matmul) over the first "
                       f"{rows} of {N} output rows, {passes} passes in {t_gemv:.1f} s; elementwise steps on one "
