@@ -930,48 +930,45 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
 
   const uint32_t lane_sel = (uint32_t)colw << 3;
   const char *lut_b = reinterpret_cast<const char *>(lut);
-  auto decode = [&](const BR &b, bf16x8_t (&bf)[2][4]) {
+  auto scale_of = [&](const BR &b, int j) __attribute__((always_inline)) {
+    return DQ ? code2[b.q[j] & 255u] * b.s[j] + offset : b.s[j];
+  };
+  // table reads of decode chunk c = 4 j + t (weights (j, t): bytes 4 t .. 4 t + 3
+  // of column j, k 32 h + 8 t .. + 7)
+  auto tread = [&](const BR &b, int c, float2 (&tv)[4]) __attribute__((always_inline)) {
+    const uint4 wv = b.w[c >> 2];
+    const int t = c & 3;
+    const uint32_t w = t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // the 16 table reads of the column first, then the arithmetic
-      float2 tv[16];
-#pragma unroll
-      for (int bb = 0; bb < 16; ++bb) {
-        const uint32_t w = bb < 4 ? b.w[j].x : bb < 8 ? b.w[j].y : bb < 12 ? b.w[j].z : b.w[j].w;
-        const uint32_t addr = __builtin_amdgcn_perm(w, lane_sel, 0x0c0c0000u | ((4u + (bb & 3)) << 8));
-        tv[bb] = *reinterpret_cast<const float2 *>(lut_b + addr);
-      }
-      const float a = DQ ? code2[b.q[j] & 255u] * b.s[j] + offset : b.s[j];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {  // MFMA t: bytes 4 t .. 4 t + 3 (k 32 h + 8 t .. + 7)
-        uint32_t o[4];
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) o[bb] = cvt_pair<ADT>(tv[4 * t + bb].x * a, tv[4 * t + bb].y * a);
-        bf[j][t] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-      }
+    for (int bb = 0; bb < 4; ++bb) {
+      const uint32_t addr = __builtin_amdgcn_perm(w, lane_sel, 0x0c0c0000u | ((4u + bb) << 8));
+      tv[bb] = *reinterpret_cast<const float2 *>(lut_b + addr);
     }
   };
-  auto mma = [&](const uint4 *stage, const bf16x8_t (&bf)[2][4]) {
+  auto cvt4 = [&](const float2 (&tv)[4], float a) __attribute__((always_inline)) {
+    uint32_t o[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = 4 * h + t;  // this lane's 16-byte chunk of the row for MFMA t
-      bf16x8_t af[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 32 * i + colw;
-        af[i] = __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ ((r >> 1) & 7))]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<ADT>(af[i], bf[j][t], acc[i][j]);
-    }
+    for (int bb = 0; bb < 4; ++bb) o[bb] = cvt_pair<ADT>(tv[bb].x * a, tv[bb].y * a);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
   };
-  // iteration kt: A(kt) in stage kt % 3, B(kt) in register set kt % 3, both
-  // loaded two k-tiles ahead (loads complete in order, so the wait for a
-  // k-tile's weights also waits for everything issued before them: with two
-  // k-tiles between issue and use neither stream stalls the step)
-  auto step = [&](int kt, uint4 *sa_cur, uint4 *sa_next2, BR &bcur, BR &bnext2) {
+  bf16x8_t bfc[2][4], bfn[2][4];  // decoded weights of k-tiles kt and kt + 1
+  {  // k-tile 0, before the loop
+    const float a[2] = {scale_of(br0, 0), scale_of(br0, 1)};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float2 tv[4];
+      tread(br0, c, tv);
+      bfc[c >> 2][c & 3] = cvt4(tv, a[c >> 2]);
+    }
+  }
+  // iteration kt: A(kt) in stage kt % 3, the weights of k-tile kt decoded by
+  // the previous iteration; B(kt + 1) in register set (kt + 1) % 3 is decoded
+  // here, cut into 8 chunks, each placed between 4 of the 32 MFMAs of k-tile
+  // kt (a chunk's 4 table reads are issued two chunks ahead) so that the
+  // decode arithmetic and table reads overlap the matrix cores; A and B are
+  // loaded two k-tiles ahead (loads complete in order, so the wait for one
+  // k-tile also waits for everything issued before it)
+  auto step = [&](int kt, uint4 *sa_cur, uint4 *sa_next2, const BR &bnext1, BR &bnext2) __attribute__((always_inline)) {
     // A(kt) must have landed for every wave: this wave's loads issued since
     // are B(kt), A(kt + 1) and B(kt + 1) (4 + 2 x (2 + 4), or 2 + 2 per B
     // without double quantization)
@@ -980,20 +977,51 @@ __global__ __launch_bounds__(256, 1) void gemm_4bit_rb_kernel(
     __syncthreads();  // and every wave is done with stage (kt + 2) % 3
     issue_a(kt + 2, sa_next2);
     issue_b(kt + 2, bnext2);
-    bf16x8_t bf[2][4];
-    decode(bcur, bf);
-    mma(sa_cur, bf);
+    const float a[2] = {scale_of(bnext1, 0), scale_of(bnext1, 1)};
+    float2 tv[8][4];
+    tread(bnext1, 0, tv[0]);
+    tread(bnext1, 1, tv[1]);
+    bf16x8_t af[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 4 * h + t;  // this lane's 16-byte chunk of the row for MFMA t
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + colw;
+        af[t][i] = __builtin_bit_cast(bf16x8_t, sa_cur[r * 8 + (c ^ ((r >> 1) & 7))]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // scheduling fence: keeps each chunk's decode beside its 4 MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 2 < 8) tread(bnext1, c + 2, tv[c + 2]);
+      const int t = c >> 1;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int i = 2 * (c & 1) + ii;
+          acc[i][j] = mfma16<ADT>(af[t][i], bfc[j][t], acc[i][j]);
+        }
+      bfn[c >> 2][c & 3] = cvt4(tv[c], a[c >> 2]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bfc[j][t] = bfn[j][t];
   };
   int kt = 0;
   for (; kt + 3 <= KT; kt += 3) {
-    step(kt, st0, st2, br0, br2);
-    step(kt + 1, st1, st0, br1, br0);
-    step(kt + 2, st2, st1, br2, br1);
+    step(kt, st0, st2, br1, br2);
+    step(kt + 1, st1, st0, br2, br0);
+    step(kt + 2, st2, st1, br0, br1);
   }
   {  // the remaining 0..2 k-tiles (kt is a multiple of 3 here)
     const int rem = KT - kt;
-    if (rem > 0) step(kt, st0, st2, br0, br2);
-    if (rem > 1) step(kt + 1, st1, st0, br1, br0);
+    if (rem > 0) step(kt, st0, st2, br1, br2);
+    if (rem > 1) step(kt + 1, st1, st0, br2, br0);
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no LDS-direct load outlives the kernel
 
