@@ -1107,10 +1107,12 @@ static hipError_t launch_gemm_t(const void *A, int64_t M, int64_t N, int64_t K,
   hipLaunchKernelGGL((gemm_4bit_narrow_kernel<ADT, CDT, DQV, MPV, NBV, KWV>), sgrid, dim3(64 * KWV), \
                      0, st, a, M, N, K, packed, sc, log2bs, table, C, bias)
     // waves per workgroup splitting K: more when the N / 32 workgroups leave
-    // compute units with few waves (8192 columns: one workgroup per CU), as
-    // long as every wave still gets a few 128-k groups
+    // compute units without a second workgroup (8192 columns: one per CU),
+    // as long as every wave still gets a few 128-k groups; with more
+    // workgroups than CUs, 4 waves (14336 x 4096: 14.3 us at M = 8 against
+    // 15.2 with 8 waves, 18.1 against 21.6 at M = 16)
     const int64_t cus = device_cu_count(), groups = (K / 64 + 1) / 2;
-    const int kw = (g.gx <= cus && groups >= 32) ? 16 : ((g.gx <= 2 * cus && groups >= 16) ? 8 : 4);
+    const int kw = g.gx > cus ? 4 : (groups >= 32 ? 16 : (groups >= 16 ? 8 : 4));
 #define QMV_NM(CDT, DQV)                                                        \
   if (M <= 8) {                                                                 \
     if (kw == 16) { QMV_N(CDT, DQV, 8, 2, 16); }                                \

@@ -210,16 +210,17 @@ def test_gemm_narrow_identity_rows_exact(qt, rows):
     assert np.array_equal(Cb, O.f32_to_bf16_bits(want))
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 1000, 4096), (3, 8200, 4160), (12, 2000, 2048), (16, 640, 8192),
-                                   (8, 256, 1024)])
+@pytest.mark.parametrize("M,N,K", [(5, 1000, 4096), (3, 8200, 4160), (6, 1000, 2048), (12, 2000, 2048),
+                                   (16, 640, 8192), (8, 256, 1024)])
 @pytest.mark.parametrize("dq", [False, True])
 def test_gemm_narrow_many_waves(M, N, K, dq):
-    """When N / 32 workgroups leave compute units with few waves the narrow
-    kernel splits K over 8 or 16 waves per workgroup: 16 waves (32 or 20
-    column groups with 32 or 64 groups of 128 k-values), 8 waves (257
-    workgroups, K = 4160 ending on half a group; 16 rows with 16 groups),
-    and 4 waves where K is too short to share (8 column groups, 16 k-groups
-    but 16 waves would get one each)."""
+    """When the N / 32 workgroups leave compute units without a second one,
+    the narrow kernel splits K over 8 or 16 waves per workgroup: 16 waves
+    (8-row tile, 32 column groups with 32 groups of 128 k-values), 8 waves
+    (8-row tile, 32 column groups with 16 k-groups; 16-row tile, 63 or 20
+    column groups with 16 or 64 k-groups); 4 waves with more workgroups than
+    compute units (257 workgroups, K = 4160 ending on half a group) and where
+    K is too short to share (8 column groups with 8 k-groups)."""
     W = gaussian((N, K), 0.02, 3 * M + N + dq, "bf16")
     A = gaussian((M, K), 1.0, M + K + 1, "bf16")
     p_ref, ahat = oracle_state(f64(W), 64, "nf4", dq)
