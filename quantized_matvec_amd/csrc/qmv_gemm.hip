@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_narrow_kernel(
   constexpr int ACH = 16 * MP;          // activation chunks per group (MP rows x 128 k-values)
   constexpr int WND = WCH / 64, AND = ACH / 64;  // LDS-direct loads per group
   constexpr int SLOT = WCH + ACH + 1;   // + the zero chunk
-  constexpr int RR = MP / 2;            // accumulator registers holding rows < MP
+  constexpr int RR = MP < 8 ? 4 : MP / 2;  // accumulator registers holding rows < MP (lanes 0..31 hold rows 0..3)
   constexpr int PER = WND + AND + (DQ ? 4 : 2);  // loads per group
   static_assert(MP % 4 == 0 && MP <= 16 && NB >= 2 && NB <= 8 && (NB - 1) * PER < 64 && KW >= 4,
                 "narrow gemm shape");
