@@ -89,12 +89,16 @@ __device__ __forceinline__ double qb_key_low(int k) {
 // One range of n for tables other than the linear one (n' = x * rcp(absmax)
 // in fp32 is within 2^-22 of n, relative): g = number of midpoints under the
 // range widened by 2^-20 of its edges; hi = the top of an interval of doubt
-// [hi - 2^-17 |hi|, hi] that covers mf -+ 2^-18 |mf|, mf the one midpoint
-// inside the widened range rounded to fp32 (n' outside it is on the same
-// side of mf as n is of the exact midpoint: both errors together are under
-// 2^-21 |mf|); hi = FLT_MAX when the range holds no midpoint (n' is always
-// below), NaN when it holds several (and for the range around zero when it
-// holds any: there n' may be subnormal, without a relative bound).
+// [hi - 2^-19 |hi|, hi] that covers mf -+ 2^-20 |mf| (each bound rounded
+// once: still beyond mf -+ 2^-21 |mf|), mf the one midpoint inside the
+// widened range rounded to fp32 (n' outside it is on the same side of mf as
+// n is of the exact midpoint: both errors together are under 2^-21 |mf|);
+// hi = FLT_MAX when the range holds no midpoint (n' is always below), NaN
+// when it holds several (and for the range around zero when it holds any:
+// there n' may be subnormal, without a relative bound).  An element in
+// doubt in a range with one midpoint has code g or g + 1: its exact n lies
+// inside the widened range, above the g midpoints below it and below the
+// ones above it, so one exact test against midpoint g decides.
 struct alignas(8) QbRange {
   float hi;
   int g;
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
         hi_d = 3.4028234663852886e38f;  // n' is always below the interval
       } else if (inside == 1 && i != 0) {
         const float mf = (float)th[g].mid;
-        hi_d = mf + fabsf(mf) * 0x1p-18f;  // the interval covers mf -+ 2^-18 |mf|
+        hi_d = mf + fabsf(mf) * 0x1p-20f;  // the interval covers mf -+ 2^-20 |mf|
       } else {
         hi_d = __builtin_nanf("");  // never decided
       }
@@ -324,8 +328,8 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
         }
       } else {
         // the code is g, or g + 1 when n' is above the range's interval of
-        // doubt [hi - 2^-17 |hi|, hi]; n' inside it (or a NaN range) takes the
-        // exact search
+        // doubt [hi - 2^-19 |hi|, hi]; n' inside it takes one exact test
+        // against midpoint g, a NaN range (or a rescaled block) the search
         float nn[VE];
         bool any = false;
 #pragma unroll
@@ -333,16 +337,20 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
           nn[j] = v[r][j] * rc;
           const QbRange e = ranges[qb_key(nn[j])];
           c[j] = e.g + (nn[j] > e.hi ? 1 : 0);
-          any |= !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-17f, fabsf(e.hi), e.hi));
+          any |= !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-19f, fabsf(e.hi), e.hi));
         }
         if (__builtin_amdgcn_ballot_w64(any) != 0) {
           const float rc2 = mr > 0.f ? __builtin_amdgcn_rcpf(mr * up) : 0.f;
 #pragma unroll
           for (int j = 0; j < VE; ++j) {
             const QbRange e = ranges[qb_key(nn[j])];
-            const bool u = !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-17f, fabsf(e.hi), e.hi));
-            if (__builtin_amdgcn_ballot_w64(u) != 0 && u)
-              c[j] = qb_search(th, (double)v[r][j], sd, ranges[qb_key((v[r][j] * up) * rc2)].g);
+            const bool u = !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-19f, fabsf(e.hi), e.hi));
+            if (__builtin_amdgcn_ballot_w64(u) != 0 && u) {
+              if (up == 1.f && e.hi == e.hi)  // one midpoint inside, unscaled key
+                c[j] = e.g + (qb_above(th[e.g], (double)v[r][j], sd) ? 1 : 0);
+              else
+                c[j] = qb_search(th, (double)v[r][j], sd, ranges[qb_key((v[r][j] * up) * rc2)].g);
+            }
           }
         }
       }
