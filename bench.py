@@ -219,6 +219,29 @@ def _auto_timed(fn, stream, torch, target_us=30000.0, lo=20, hi=600):
     return timed_loop(fn, iters, stream, torch), iters
 
 
+def graph_interval(fn, stream, torch, nodes=230, reps=15):
+    """Microseconds per launch of fn(0 .. nodes - 1) captured once into a HIP
+    graph and replayed reps times back to back: the GPU's own interval
+    between consecutive launches, free of the host's per-call cost."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(nodes):
+            fn(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            g.replay()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+    end.synchronize()
+    del g
+    return start.elapsed_time(end) / (reps * nodes) * 1e3
+
+
 def _ok(rc):
     if rc != 0:
         from quantized_matvec_amd import qmv
@@ -357,7 +380,7 @@ def measured_ceilings(torch, dev, reps=20):
     from quantized_matvec_amd import qmv
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
     out = {}
     for name, fn, nbytes in (("read_gbs", lambda: qmv.stream_read(src, sink), COPY_BYTES),
                              ("write_gbs", lambda: dst.fill_(1.0), COPY_BYTES),
@@ -613,9 +636,27 @@ def main():
             return L.qmv_embedding_4bit(eidx.data_ptr(), EMB_T, EMB_V, K, pe.data_ptr(), ctypes.byref(ec), BS, 0,
                                         eout.data_ptr(), 2, s_h)
 
+        # context for the gemv's figure: a plain 128-bit read of each rotating
+        # copy's packed bytes (the same size, launched the same way), and the
+        # interval of back-to-back launches that do almost nothing (one
+        # workgroup reading 16 bytes), replayed from a HIP graph so that the
+        # host's cost per call (about 3.5 us through ctypes) does not set it
+        rsink = torch.zeros(8192, dtype=torch.int32, device=dev)
+        pk_bytes = N * K // 2
+
+        def run_read_same(i):
+            return L.qmv_stream_read(p_ptr[i % n_p], pk_bytes, rsink.data_ptr(), s_h)
+
+        def run_floor(i):
+            return L.qmv_stream_read(p_ptr[0], 16, rsink.data_ptr(), s_h)
+
+        _ok(run_floor(0))
+        floor_graph_us = graph_interval(run_floor, stream, torch)
+        gemv_graph_us = graph_interval(run_gemv, stream, torch)
+
         # each loop runs about 30 ms of launches (a short loop right after a
         # memory-bound one reads a compute-bound kernel up to 15 % slow)
-        for name, fn in (("gemv_4bit", run_gemv), ("gemm_4bit", run_gemm), ("gemm_4bit_backward", run_bwd),
+        for name, fn in (("gemv_4bit", run_gemv), ("read_same_bytes", run_read_same), ("gemm_4bit", run_gemm), ("gemm_4bit_backward", run_bwd),
                          ("dequantize_4bit", run_deq), ("quantize_4bit", run_quant), ("double_quant", run_dq),
                          ("quantize_blockwise", run_q8), ("quantize_blockwise_dynamic", lambda i: run_q8(i, tree_p)),
                          ("dequantize_blockwise", run_dq8), ("embedding_4bit", run_emb)):
@@ -623,6 +664,7 @@ def main():
             kern[name] = us
             kern_iters[name] = it
 
+    read_same_us = kern.pop("read_same_bytes")
     rep = {}
     for name, us in kern.items():
         e = {"us_per_launch": round(us, 3), "launches_timed": kern_iters[name]}
@@ -666,6 +708,14 @@ def main():
                      "traffic": traffic, "kernel": "gemv_4bit",
                      "algorithmic_bytes_per_launch": ab["gemv_4bit"], "avg_launch_us": round(gemv_us, 3),
                      "frac_of_measured_read": round(gemv_gbs / ceil["read_gbs"], 4),
+                     # the gemv's rate against a plain read of the same packed
+                     # weight (29.4 MB per launch, same rotation and loop); the
+                     # gemv's interval when its launches are replayed from a HIP
+                     # graph; the interval below which no launch goes
+                     "same_size_read_us": round(read_same_us, 3),
+                     "frac_of_same_size_read": round(gemv_gbs / (N * K // 2 / read_same_us / 1e3), 4),
+                     "graph_replay_us": round(gemv_graph_us, 3),
+                     "launch_interval_floor_us": round(floor_graph_us, 3),
                      "note": "avg_launch_us is the interval between back-to-back launches (HIP events around "
                              "the whole loop); a rocprofv3 kernel trace reports the kernel's own duration, "
                              "shorter by the dispatch gap between consecutive kernels"},

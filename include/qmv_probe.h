@@ -15,15 +15,18 @@ extern "C" {
 #endif
 
 /*
- * stream_read: reads every byte of p once with 128-bit loads (a grid-stride
- * pass over the whole buffer by at most 1024 workgroups) and XORs the 32-bit
- * words each workgroup read into its own word of sink, so the reads cannot
- * be elided and no two workgroups touch one address; timed over a buffer
- * much larger than the caches it gives the streaming-read ceiling.  The XOR
- * of the 1024 sink words is the XOR of every word of p.
+ * stream_read: reads every byte of p once with 128-bit loads and XORs the
+ * 32-bit words each workgroup read into its own word of sink, so the reads
+ * cannot be elided and no two workgroups touch one address.  Up to 32 MB
+ * every thread reads one 16-byte chunk (all loads in flight at once, up to
+ * 8192 workgroups); a larger buffer is read in a grid-stride pass by at most
+ * 1024 workgroups.  Timed over a buffer much larger than the caches it gives
+ * the streaming-read ceiling, over a smaller one the time a plain read of
+ * that many bytes takes.  The XOR of the 8192 sink words is the XOR of every
+ * word of p.
  *   p       device, 16-byte aligned (QMV_ERR_ALIGNMENT), bytes > 0 and a
  *           multiple of 16 (QMV_ERR_INVALID_ARG)
- *   sink    device uint32 [1024], 4-byte aligned; XORed into, not cleared:
+ *   sink    device uint32 [8192], 4-byte aligned; XORed into, not cleared:
  *           the caller zeroes it to read the checksum.  Concurrent calls on
  *           one sink race.
  *   stream  hipStream_t; the call only enqueues.

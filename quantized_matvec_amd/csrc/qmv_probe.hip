@@ -35,9 +35,16 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4 
   }
 }
 
+// Up to 32 MB every thread reads one chunk (all loads in flight at once,
+// which reads a buffer of that size fastest; at most 8192 workgroups, one
+// sink word each); beyond, at most 1024 workgroups stride over the buffer
+// (the faster form for gigabytes).
+constexpr int64_t kProbeOnePassChunks = int64_t(1) << 21;
+
 hipError_t launch_stream_read(const void *p, int64_t bytes, uint32_t *sink, hipStream_t st) {
   const int64_t n16 = bytes / 16;
   int64_t grid = std::min<int64_t>(4 * (int64_t)device_cu_count(), kProbeMaxGrid);
+  if (n16 <= kProbeOnePassChunks) grid = n16;  // then divided by the threads per workgroup
   grid = std::min<int64_t>(grid, (n16 + kProbeThreads - 1) / kProbeThreads);
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, st,
                      static_cast<const uint4 *>(p), n16, sink);

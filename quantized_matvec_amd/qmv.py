@@ -426,16 +426,16 @@ def default_code2() -> list:
 def stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
     """Measurement probe (qmv_stream_read): reads every byte of the contiguous
     device tensor `buf` once with 128-bit loads; workgroup b XORs the 32-bit
-    words it read into sink[b] (sink: 1024 int32 on the device, zeroed here
+    words it read into sink[b] (sink: 8192 int32 on the device, zeroed here
     when not given; the XOR of all of it is the XOR of buf's words).
     Returns the sink; nothing synchronizes."""
     if not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("stream_read: buf must be a contiguous device tensor")
     nbytes = buf.numel() * buf.element_size()
     if sink is None:
-        sink = torch.zeros(1024, dtype=torch.int32, device=buf.device)
-    if sink.numel() < 1024 or sink.dtype != torch.int32 or not sink.is_cuda:
-        raise ValueError("stream_read: sink must be 1024 int32 on the device")
+        sink = torch.zeros(8192, dtype=torch.int32, device=buf.device)
+    if sink.numel() < 8192 or sink.dtype != torch.int32 or not sink.is_cuda:
+        raise ValueError("stream_read: sink must be 8192 int32 on the device")
     _check(lib().qmv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)),
            "stream_read")
     return sink
