@@ -522,6 +522,43 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
         }
       }
     }
+  } else if (MR <= 2 && XLDS && nrows >= 2) {
+    // one or two activation rows too long for registers: weight rows in
+    // pairs, slice by slice, so that each slice's activations are read from
+    // LDS once for two items; item (2 p + r, s) decodes from slot r.  An odd
+    // last row is paired with a dead one (its loads move nothing, its sums
+    // are dropped).
+    const int64_t np = (nrows + 1) >> 1;
+    float acc2[2][MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc2[0][m] = acc2[1][m] = 0.f;
+    for (int64_t p = 0; p < np; ++p) {
+      const bool two = 2 * p + 1 < nrows;
+      for (int s = 0; s < S; ++s) {
+        uint4v xq[MR][4];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xq[m][q] = xlv[m * rch + s * 256 + q * 64 + lane];
+        issue(2 * p + 1, s, two, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        float a = item_scale(sq[0], sa[0]);
+        decode(w[0], xq, part);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc2[0][m] = fmaf(a, part[m], acc2[0][m]);
+        const bool more = s + 1 < S;
+        issue(more ? 2 * p : 2 * p + 2, more ? s + 1 : 0, more || p + 1 < np, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        a = item_scale(sq[1], sa[1]);
+        decode(w[1], xq, part);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc2[1][m] = fmaf(a, part[m], acc2[1][m]);
+      }
+      finish_row(2 * p, acc2[0]);
+      if (two) finish_row(2 * p + 1, acc2[1]);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc2[0][m] = acc2[1][m] = 0.f;
+    }
   } else {
     int64_t rd = 0, rn = 0;  // row (within the run) of the item decoded / issued next
     int sd = 0, sn = 1;      // and its slice

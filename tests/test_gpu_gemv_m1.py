@@ -33,6 +33,8 @@ CASES = [
     (100, 4096, 64, True),      # fewer rows than waves: most waves have no row
     (1, 4096, 64, False),       # a single row
     (9, 6144, 2048, True),      # three slices per row, one block per slice
+    (4101, 8256, 64, True),     # activations from LDS, rows taken in pairs on the waves with two
+    (12290, 8224, 32, False),   # three rows per wave: the last one paired with a dead row
 ]
 
 
