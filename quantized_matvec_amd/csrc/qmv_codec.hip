@@ -52,17 +52,20 @@ __device__ __forceinline__ uint32_t rank_to_code(int r) {
 // means x > a m_j (a tie stays with the smaller magnitude) and above a
 // negative one x >= a m_j.
 //
-// The rank is read off a bin position.  t = S x / a + O is approximated in
-// fp32 as fma(x, S rcp(a), O); bin = floor(t).  The host picks S and O so
-// that every bin holds at most one midpoint, none within 0.02 of a bin edge,
-// and tabulates per bin J(b) = the midpoints below it and pos(b) = S m_J + O
-// for the midpoint inside it (+inf when there is none).  Then
+// The rank is read off a bin position.  u = S x / a + O; bin = floor(u).  The
+// host picks S and O so that every bin holds at most one midpoint, none
+// within 0.02 of a bin edge, and tabulates per bin J(b) = the midpoints below
+// it and pos(b) = S m_J + O - 1/2 for the midpoint inside it (+inf when there
+// is none).  The kernel computes t = u - 1/2 in fp32 as fma(x, S rcp(a),
+// O - 1/2), takes the bin as t rounded to the nearest integer (one
+// conversion, saturated), and
 //   rank = J(b) + [t > pos(b)].
-// The fp32 t is within 1e-5 of the exact S x / a + O (rcp is within an ulp,
-// the rest one rounding each; |t| < 64) and pos(b) within 2e-6 of the exact
-// S m_J + O, so whenever |t - pos(b)| >= 2^-15 the comparison has the exact
-// answer; an element whose approximate t falls in a neighbouring bin sits
-// within 1e-5 of a bin edge, where no midpoint is, so the count is the same.
+// The fp32 t is within 1e-5 of the exact u - 1/2 (rcp is within an ulp, the
+// rest one rounding each; |t| < 64) and pos(b) within 2e-6 of the exact
+// S m_J + O - 1/2, so whenever |t - pos(b)| >= 2^-15 the comparison has the
+// exact answer; an element whose approximate t falls in a neighbouring bin
+// sits within 1e-5 of a bin edge, where no midpoint is, so the count is the
+// same.
 // The few elements inside the 2^-15 band (exact ties among them) are decided
 // exactly in float64: a m_J is exact there (24 x 29 significant bits), as is
 // the comparison with x.
@@ -72,9 +75,9 @@ constexpr float kQBand = 0x1p-15f;  // certificate band around a midpoint, in bi
 struct QuantArgs {
   Midpoints4 mids;
   uint8_t cand[256];     // J(b); bins 64 .. 255 count every midpoint
-  float pos[256];        // pos(b), +inf for a bin without a midpoint
+  float pos[256];        // pos(b) (less 1/2), +inf for a bin without a midpoint
   float bin_scale;       // S
-  float bin_offset;      // O
+  float bin_offset;      // O - 1/2
 };
 
 template <int DT, int QT, int E>
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
 
     // t = S x / a + O: tiny blocks are scaled up by 2^100 (exact) so the
     // reciprocal stays finite, huge ones down by 2^100 so it stays normal;
-    // an all-zero block has t = O, the position of 0
+    // an all-zero block has t = O - 1/2, the position of 0
     const float sc = m < 0x1p-100f ? 0x1p100f : (m > 0x1p100f ? 0x1p-100f : 1.f);
     const float inv = m > 0.f ? qa.bin_scale * __builtin_amdgcn_rcpf(m * sc) : 0.f;
     const float O = qa.bin_offset;
@@ -165,22 +168,26 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
     float pb[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const uint32_t b = (uint32_t)tq[i];  // floor: t >= 1 (clamped into the table)
-      J[i] = (int)cand[b & 255u];
-      pb[i] = pos[b & 255u];
+      // the bin: t carries the offset O - 1/2, so rounding to the nearest
+      // integer (saturated to 0 .. 255, NaN to 0) is the floor of S x / a + O;
+      // where the rounding and the floor can differ, t is within an ulp of a
+      // bin edge, and either neighbouring bin gives the same rank
+      const uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32(tq[i], 0, 0u);
+      J[i] = (int)cand[b];
+      pb[i] = pos[b];
     }
     uint32_t rank[E];
-    uint32_t amb = 0;
+    bool amb = false;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       rank[i] = (uint32_t)J[i] + (tq[i] > pb[i] ? 1u : 0u);
-      amb |= (fabsf(tq[i] - pb[i]) < kQBand ? 1u : 0u) << i;
+      amb |= fabsf(tq[i] - pb[i]) < kQBand;
     }
-    if (__builtin_amdgcn_ballot_w64(amb != 0) != 0) {  // rare: decide the band exactly
+    if (__builtin_amdgcn_ballot_w64(amb) != 0) {  // rare: decide the band exactly
       const double ad = (double)m;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
-        if ((amb >> i) & 1u) {
+        if (fabsf(tq[i] - pb[i]) < kQBand) {
           const double mid = mids[J[i]];
           const double p = ad * mid;  // exact
           const double xd = (double)v[i];
@@ -293,10 +300,14 @@ static bool bin_geometry(const Midpoints4 &m, int nt, QuantArgs &qa) {
     for (int j = 0; j < nt; ++j)
       c += std::floor((double)qa.bin_scale * m.mid[j] + (double)qa.bin_offset) < b ? 1 : 0;
     qa.cand[b] = (uint8_t)c;
-    // the midpoint inside bin b, if any, is midpoint c
+    // the midpoint inside bin b, if any, is midpoint c; its position is kept
+    // less 1/2, like t (below)
     const double pj = c < nt ? (double)qa.bin_scale * m.mid[c] + (double)qa.bin_offset : 0.0;
-    qa.pos[b] = (c < nt && std::floor(pj) == (double)b) ? (float)pj : INFINITY;
+    qa.pos[b] = (c < nt && std::floor(pj) == (double)b) ? (float)(pj - 0.5) : INFINITY;
   }
+  // the kernels compute t = S x / a + O - 1/2 and take the bin as t rounded
+  // to the nearest integer (O - 1/2 has 8 fraction bits: exact in fp32)
+  qa.bin_offset -= 0.5f;
   return true;
 }
 
