@@ -8,11 +8,12 @@
 // as dequantize_4bit returns those elements: fp32(T[code] * a_hat) rounded to
 // the output type.  An index outside [0, V) yields a row of zeros.
 //
-// A workgroup of 256 threads writes a 2048-element segment of one output row
-// (grid: row segments x output rows).  When D is a multiple of 8, thread t of
-// the segment decodes 8 elements from one 4-byte load (one block: blocks are
-// at least 32 and aligned) and writes them with one 16-byte (or two, fp32)
-// store; otherwise each thread decodes single elements.
+// A workgroup of 256 threads writes a 2048-element segment of output rows
+// (grid: row segments x groups of rows).  When D is a multiple of 8, thread t
+// of the segment decodes 8 elements from one 4-byte load (one block: blocks
+// are at least 32 and aligned) and writes them with one 16-byte (or two,
+// fp32) store, for 4 rows at a time whose loads are all issued first;
+// otherwise each thread decodes single elements of one row at a time.
 #include <algorithm>
 
 #include "qmv_launch.hpp"
@@ -22,6 +23,7 @@
 namespace qmv {
 
 constexpr int kEmbSeg = 2048;  // elements of a row per workgroup
+constexpr int kEmbTok = 4;     // tokens per pass of a workgroup (D a multiple of 8)
 
 template <int QT, int ODT, bool DQ, bool VEC>
 __global__ __launch_bounds__(256) void embedding_4bit_kernel(const int64_t *__restrict__ idx,
@@ -41,38 +43,65 @@ __global__ __launch_bounds__(256) void embedding_4bit_kernel(const int64_t *__re
   const int64_t d0 = (int64_t)blockIdx.x * kEmbSeg;
   const float offset = DQ ? sc.offset[0] : 0.f;
 
+  if constexpr (VEC) {
+    // kEmbTok tokens per pass: their indices, then all their codes and
+    // scales are requested before any is used, so the dependent loads
+    // (index -> code and scale code -> table entry) of the tokens overlap
+    const int64_t d = d0 + 8 * (int64_t)tid;
+    for (int64_t t0 = (int64_t)blockIdx.y * kEmbTok; t0 < T; t0 += (int64_t)gridDim.y * kEmbTok) {
+      int64_t row[kEmbTok];
+      bool valid[kEmbTok];
+#pragma unroll
+      for (int k = 0; k < kEmbTok; ++k) {
+        row[k] = t0 + k < T ? idx[t0 + k] : -1;     // the same for the whole workgroup
+        valid[k] = row[k] >= 0 && row[k] < V && d < D;
+      }
+      uint32_t w[kEmbTok];
+      float a[kEmbTok];
+#pragma unroll
+      for (int k = 0; k < kEmbTok; ++k) {
+        w[k] = 0u;
+        a[k] = 0.f;
+        if (valid[k]) {
+          const int64_t e = row[k] * D + d;        // a multiple of 8: one block, 4 aligned bytes
+          w[k] = *reinterpret_cast<const uint32_t *>(packed + (e >> 1));
+          a[k] = block_scale<DQ>(sc, e >> log2bs, offset);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kEmbTok; ++k) {
+        if (t0 + k >= T || d >= D) continue;
+        float v[8];
+        if (valid[k]) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const float2 tv = lut2[(w[k] >> (8 * b)) & 0xffu];
+            v[2 * b] = tv.x * a[k];
+            v[2 * b + 1] = tv.y * a[k];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        }
+        OT *dst = out + (t0 + k) * D;
+        if constexpr (ODT == kF32) {
+          float4 *o = reinterpret_cast<float4 *>(dst + d);
+          o[0] = make_float4(v[0], v[1], v[2], v[3]);
+          o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          *reinterpret_cast<uint4 *>(dst + d) =
+              make_uint4(cvt_pair<ODT>(v[0], v[1]), cvt_pair<ODT>(v[2], v[3]),
+                         cvt_pair<ODT>(v[4], v[5]), cvt_pair<ODT>(v[6], v[7]));
+        }
+      }
+    }
+    return;
+  }
   for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
     const int64_t row = idx[t];                       // the same for the whole workgroup
     const bool valid = row >= 0 && row < V;
     OT *dst = out + t * D;
-    if constexpr (VEC) {
-      const int64_t d = d0 + 8 * (int64_t)tid;
-      if (d >= D) continue;
-      float v[8];
-      if (valid) {
-        const int64_t e = row * D + d;                // a multiple of 8: one block, 4 aligned bytes
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(packed + (e >> 1));
-        const float a = block_scale<DQ>(sc, e >> log2bs, offset);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float2 tv = lut2[(w >> (8 * b)) & 0xffu];
-          v[2 * b] = tv.x * a;
-          v[2 * b + 1] = tv.y * a;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-      }
-      if constexpr (ODT == kF32) {
-        float4 *o = reinterpret_cast<float4 *>(dst + d);
-        o[0] = make_float4(v[0], v[1], v[2], v[3]);
-        o[1] = make_float4(v[4], v[5], v[6], v[7]);
-      } else {
-        *reinterpret_cast<uint4 *>(dst + d) =
-            make_uint4(cvt_pair<ODT>(v[0], v[1]), cvt_pair<ODT>(v[2], v[3]),
-                       cvt_pair<ODT>(v[4], v[5]), cvt_pair<ODT>(v[6], v[7]));
-      }
-    } else {
+    {
       const int64_t d_end = std::min<int64_t>(D, d0 + kEmbSeg);
       for (int64_t d = d0 + tid; d < d_end; d += 256) {
         float v = 0.f;
@@ -104,7 +133,8 @@ hipError_t launch_embedding_4bit(const int64_t *idx, int64_t T, int64_t V, int64
                                  const uint8_t *packed, const Scales &sc, bool dq, int log2bs,
                                  int qt, void *out, int out_dtype, hipStream_t st) {
   const bool vec = D % 8 == 0;
-  const dim3 grid((unsigned)((D + kEmbSeg - 1) / kEmbSeg), (unsigned)std::min<int64_t>(T, 65535));
+  const int64_t passes = vec ? (T + kEmbTok - 1) / kEmbTok : T;
+  const dim3 grid((unsigned)((D + kEmbSeg - 1) / kEmbSeg), (unsigned)std::min<int64_t>(passes, 65535));
 #define QMV_E(QTV, ODTV)                                                                     \
   if (dq) launch_emb_t<QTV, ODTV, true>(vec, grid, idx, T, V, D, packed, sc, log2bs, out, st); \
   else launch_emb_t<QTV, ODTV, false>(vec, grid, idx, T, V, D, packed, sc, log2bs, out, st)
