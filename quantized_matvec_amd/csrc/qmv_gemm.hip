@@ -253,7 +253,7 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void gemm_4bit_kernel(co
 // on the order of its terms, and A is read in the same order), so every
 // operand is a contiguous 16 bytes.  The weights are dequantized in registers
 // exactly as in the tile kernel (fp32(T * a_hat) rounded to bf16).  The next
-// step's loads are issued before the current step is computed.
+// two steps' loads are issued before the current step is computed.
 // ---------------------------------------------------------------------------
 template <int ADT, int CDT, bool DQ, int MT, int KW>
 __global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
@@ -347,20 +347,25 @@ __global__ __launch_bounds__(64 * KW) void gemm_4bit_skinny_kernel(
     }
   };
 
-  // two register sets: step s + KW is loaded while step s is computed.  No
-  // branch separates a load from the computation it feeds (a load that could
-  // be moved past the computation before it would be issued late).
+  // three register sets: the wave's steps i + 1 and i + 2 are in flight
+  // while step i is computed.  No branch separates a load from the
+  // computation it feeds (a load that could be moved past the computation
+  // before it would be issued late).
   const int64_t nw = nsteps > wave ? (nsteps - wave + KW - 1) / KW : 0;  // this wave's steps
-  Regs r0, r1;
+  Regs r0, r1, r2;
   load(wave, r0);
+  load(wave + KW, r1);
   int64_t i = 0;
-  for (; i + 1 < nw; i += 2) {
-    load(wave + (i + 1) * KW, r1);
+  for (; i + 2 < nw; i += 3) {
+    load(wave + (i + 2) * KW, r2);
     compute(r0);
-    load(wave + (i + 2) * KW, r0);
+    load(wave + (i + 3) * KW, r0);
     compute(r1);
+    load(wave + (i + 4) * KW, r1);
+    compute(r2);
   }
   if (i < nw) compute(r0);
+  if (i + 1 < nw) compute(r1);
 
   // sum the waves' partial tiles (wave order) and store
   if (wave > 0) {
