@@ -330,24 +330,28 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
         // the code is g, or g + 1 when n' is above the range's interval of
         // doubt [hi - 2^-19 |hi|, hi]; n' inside it takes one exact test
         // against midpoint g, a NaN range (or a rescaled block) the search
-        float nn[VE];
+        // per element: in doubt (u) and whether its range has a single
+        // midpoint (one): kept as lane masks, so the exact path below needs
+        // no second range read (an element in doubt is not above the
+        // interval, so its guess c is the range's g)
         bool any = false;
+        bool u[VE], one[VE];
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
-          nn[j] = v[r][j] * rc;
-          const QbRange e = ranges[qb_key(nn[j])];
-          c[j] = e.g + (nn[j] > e.hi ? 1 : 0);
-          any |= !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-19f, fabsf(e.hi), e.hi));
+          const float nn = v[r][j] * rc;
+          const QbRange e = ranges[qb_key(nn)];
+          c[j] = e.g + (nn > e.hi ? 1 : 0);
+          u[j] = !(nn > e.hi || nn < fmaf(-0x1p-19f, fabsf(e.hi), e.hi));
+          one[j] = e.hi == e.hi;
+          any |= u[j];
         }
         if (__builtin_amdgcn_ballot_w64(any) != 0) {
           const float rc2 = mr > 0.f ? __builtin_amdgcn_rcpf(mr * up) : 0.f;
 #pragma unroll
           for (int j = 0; j < VE; ++j) {
-            const QbRange e = ranges[qb_key(nn[j])];
-            const bool u = !(nn[j] > e.hi || nn[j] < fmaf(-0x1p-19f, fabsf(e.hi), e.hi));
-            if (__builtin_amdgcn_ballot_w64(u) != 0 && u) {
-              if (up == 1.f && e.hi == e.hi)  // one midpoint inside, unscaled key
-                c[j] = e.g + (qb_above(th[e.g], (double)v[r][j], sd) ? 1 : 0);
+            if (__builtin_amdgcn_ballot_w64(u[j]) != 0 && u[j]) {
+              if (up == 1.f && one[j])  // one midpoint inside, unscaled key
+                c[j] = c[j] + (qb_above(th[c[j]], (double)v[r][j], sd) ? 1 : 0);
               else
                 c[j] = qb_search(th, (double)v[r][j], sd, ranges[qb_key((v[r][j] * up) * rc2)].g);
             }
