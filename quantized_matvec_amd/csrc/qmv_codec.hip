@@ -18,6 +18,13 @@
 
 namespace qmv {
 
+// A 16-byte store marked non-temporal (streamed out: the output is not read
+// back by the kernel, and the hint measured faster for large outputs).
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void *p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(u32x4_nt{a, b, c, d}, static_cast<u32x4_nt *>(p));
+}
+
 
 int log2_exact(int64_t v) {
   int l = 0;
@@ -213,7 +220,8 @@ __global__ __launch_bounds__(256) void quantize_4bit_kernel(const void *__restri
       if constexpr (E == 8) {
         *reinterpret_cast<uint32_t *>(dst) = word[0];
       } else {
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(word[0], word[1]);
+        typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32x2_nt{word[0], word[1]}, reinterpret_cast<u32x2_nt *>(dst));
       }
     } else {
 #pragma unroll
@@ -877,9 +885,10 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
         o[2 * bb] = t.x * a;
         o[2 * bb + 1] = t.y * a;
       }
-      float4 *dst = reinterpret_cast<float4 *>(out + e);
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      store16_nt(out + e, __float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                 __float_as_uint(o[3]));
+      store16_nt(out + e + 4, __float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]),
+                 __float_as_uint(o[7]));
     } else {
       uint32_t o[4];
 #pragma unroll
@@ -887,7 +896,7 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
         const float2 t = lut2[(word >> (8 * bb)) & 0xffu];
         o[bb] = cvt_pair<ODT>(t.x * a, t.y * a);
       }
-      *reinterpret_cast<uint4 *>(out + e) = make_uint4(o[0], o[1], o[2], o[3]);
+      store16_nt(out + e, o[0], o[1], o[2], o[3]);
     }
   };
 
