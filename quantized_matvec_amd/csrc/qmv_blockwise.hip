@@ -371,7 +371,10 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
         word[w] = (uint32_t)c[4 * w] | ((uint32_t)c[4 * w + 1] << 8) |
                   ((uint32_t)c[4 * w + 2] << 16) | ((uint32_t)c[4 * w + 3] << 24);
       if (FULL || e0 + VE <= n) {
-        if constexpr (VE == 8) *reinterpret_cast<uint2 *>(q + e0) = make_uint2(word[0], word[1]);
+        if constexpr (VE == 8) {
+          typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(u32x2_nt{word[0], word[1]}, reinterpret_cast<u32x2_nt *>(q + e0));
+        }
         else *reinterpret_cast<uint32_t *>(q + e0) = word[0];
       } else {
 #pragma unroll
