@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
     const int64_t left = K - (int64_t)s * 2048;
     const int64_t ne = left < 2048 ? left : 2048;   // live weights of the item
     w[j] = __builtin_amdgcn_raw_buffer_load_b128(
-        make_rsrc(packed + (e0 >> 1), live ? (uint32_t)(ne >> 1) : 0u), lane_w, 0, 0);
+        make_rsrc(packed + (e0 >> 1), live ? (uint32_t)(ne >> 1) : 0u), lane_w, 0, 2);
     const int64_t ub = e0 >> log2bs;             // block of the first weight
     const int64_t ue = (e0 + ne - 1) >> log2bs;  // block of the last weight
     const uint32_t nbl = live ? (uint32_t)(ue - ub + 1) : 0u;
