@@ -213,9 +213,13 @@ __global__ __launch_bounds__(256) void quantize_blockwise_kernel(const void *__r
   const int64_t nfull = n / kQbTile;
 
   auto load_full = [&](int64_t t, uint4 (&raw)[R]) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(A + t * kQbTile) + tid;
+    typedef uint32_t u32x4_ld __attribute__((ext_vector_type(4)));
+    const u32x4_ld *src = reinterpret_cast<const u32x4_ld *>(A + t * kQbTile) + tid;
 #pragma unroll
-    for (int r = 0; r < R; ++r) raw[r] = src[r * 256];
+    for (int r = 0; r < R; ++r) {  // read once: non-temporal
+      const u32x4_ld v = __builtin_nontemporal_load(src + r * 256);
+      raw[r] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   };
   auto convert = [&](const uint4 (&raw)[R], float (&v)[R][VE]) {
 #pragma unroll

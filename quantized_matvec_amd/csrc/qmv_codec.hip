@@ -913,7 +913,7 @@ __global__ __launch_bounds__(kDeqThreads) void dequantize_4bit_kernel(
       const int64_t c = cu < nchunk ? cu : nchunk - 1;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        pw[u][w] = pk[c * 256 + 64 * w + lane];
+        pw[u][w] = __builtin_nontemporal_load(pk + c * 256 + 64 * w + lane);  // read once
         const int64_t b = ((c << 11) + 512 * w + 8 * lane) >> log2bs;
         if constexpr (DQ) {
           sq[u][w] = sc.q[b];
