@@ -297,6 +297,7 @@ __global__ __launch_bounds__(LutShape<M>::kThreads, LutShape<M>::kMinWavesPerSim
 //  * Every load is a buffer load whose range covers exactly the item's live
 //    bytes (weights, block codes, group scales); a lane past the row's last
 //    piece, or an item past the run's end, reads zeros and moves no data.
+//    The weights, read once, carry the non-temporal hint.
 //  * The activation vector is staged once in LDS (when it fits), transposed
 //    so that a slice's 64 lanes read consecutive 16-byte chunks.  With 1 to 4
 //    slices per row every lane then keeps its chunks of all slices in
@@ -366,6 +367,7 @@ __global__ __launch_bounds__(kM1Threads) void gemv_4bit_m1_kernel(
     const int64_t e0 = row * K + (int64_t)s * 2048;  // first weight of the item
     const int64_t left = K - (int64_t)s * 2048;
     const int64_t ne = left < 2048 ? left : 2048;   // live weights of the item
+    // the weights are read once: non-temporal hint (cache policy 2)
     w[j] = __builtin_amdgcn_raw_buffer_load_b128(
         make_rsrc(packed + (e0 >> 1), live ? (uint32_t)(ne >> 1) : 0u), lane_w, 0, 2);
     const int64_t ub = e0 >> log2bs;             // block of the first weight
